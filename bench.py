@@ -1,0 +1,267 @@
+"""Benchmark of the KDA token mixer on one MI355X.
+
+A step is one pass of the prefill path over the long-context workload
+(B = 1, T = 65,536, 96 heads x 128, bf16 I/O, fp32 state, chunk 64):
+kda_conv -> kda_chunk_prefill -> kda_gated_norm, inputs resident in HBM.
+``value`` is prefill tokens/s.  The decode step (B = 256, 64 consecutive
+steps) is timed in the same run and reported as TB/s under ``decode``.
+
+The roofline object describes the dominant kernel (the chunkwise recurrence):
+achieved = its algorithmic bytes per launch / its average launch duration,
+timed with HIP events on the stream it runs on.  ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode TB/s at 96x128 heads; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_T65536_traffic.json")
+CHUNK_SOURCES = [os.path.join(ROOT, "linear_attention_recurrence_09_amd", "csrc", f)
+                 for f in ("kda_chunk.hip", "kda_device.hpp")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def chunk_source_hash():
+    h = hashlib.sha256()
+    for p in CHUNK_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != chunk_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def prefill_bytes(N, H, D, n_seqs, es=2):
+    """Algorithmic HBM bytes of each prefill kernel (one launch each)."""
+    P = 3 * H * D
+    chunk = (4 * N * H * D * es          # q, k, v, g
+             + N * H * es                # beta
+             + N * H * D * es            # o
+             + n_seqs * H * D * D * 4)   # final state (no initial state here)
+    conv = 2 * N * P * es               # x in, y out
+    norm = 3 * N * H * D * es           # o, gate in, y out
+    return dict(conv=conv, chunk=chunk, norm=norm)
+
+
+def chunk_flops(N, H, D, C=64):
+    """Algorithmic FLOPs of the chunked recurrence (triangular-exact WY form)."""
+    per_token_head = 6 * D * D + (C * (C - 1) * D + 2 * C * (C + 1) * D + 2 * C * (C + 1) * D
+                                  + C ** 3 / 3) / C
+    return per_token_head * N * H
+
+
+def decode_bytes(B, H, D, es=2):
+    P = 3 * H * D
+    return (2 * B * H * D * D * 4        # state read + write
+            + 2 * B * P * 3 * es         # rolling conv state read + write
+            + B * P * es                 # new token x
+            + B * H * D * es             # g
+            + B * H * es                 # beta
+            + B * H * D * es             # o
+            + P * 4 * 4)                 # conv weights
+
+
+def cpu_baseline(inp, spec, T_s):
+    """Oracle on the first T_s tokens of as many heads as it has threads."""
+    import numpy as np
+    import torch
+    from oracle import c_oracle
+    nthr = c_oracle.num_threads()
+    H_s = min(nthr, spec.H)
+    heads = list(range(H_s))
+    H, D = spec.H, spec.D
+    cols = []
+    for part in range(3):
+        for h in heads:
+            cols.extend(range(part * H * D + h * D, part * H * D + (h + 1) * D))
+    cols_t = torch.as_tensor(cols, device=inp["x"].device)
+    f = lambda t: t.detach().double().cpu().numpy()
+    xs = f(inp["x"][:T_s].index_select(1, cols_t))
+    ws = f(inp["conv_w"].index_select(0, cols_t))
+    gs, bs, zs = f(inp["g"][:T_s, heads]), f(inp["beta"][:T_s, heads]), f(inp["gate"][:T_s, heads])
+    nw = f(inp["norm_w"])
+    t0 = time.perf_counter()
+    c_oracle.kda_prefill(xs, ws, gs, bs, zs, nw, [0, T_s], H_s, D)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": T_s * H_s / H / dt, "unit": "tokens/s", "cores": min(nthr, H_s),
+            "kind": "oracle",
+            "sample": (f"C fp64 oracle, whole prefill path (conv, L2, recurrence, gated norm) on "
+                       f"the first {T_s} tokens of {H_s} of the {H} heads, {dt:.1f} s; "
+                       f"scaled to tokens/s of the {H}-head layer")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the KDA mixer here is a single-GPU library "
+              f"(requested --gpus {args.gpus}); see the sharding notes in the design document.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_09_amd as kda
+    import synth
+
+    torch.cuda.set_device(0)
+    kda.lib()
+    spec = synth.CONFIGS[2]
+    H, D, C = spec.H, spec.D, spec.chunk
+    HD = H * D
+    log(f"drawing inputs for {spec.name}")
+    inp = synth.prefill_inputs(spec, device="cuda")
+    N = inp["x"].shape[0]
+    x, w, g, beta, gate, nw = (inp[k] for k in ("x", "conv_w", "g", "beta", "gate", "norm_w"))
+    y_qkv = torch.empty_like(x)
+    o = torch.empty((N, H, D), dtype=x.dtype, device="cuda")
+    y = torch.empty_like(o)
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+          for _ in range(args.steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        kda.kda_conv(x, w, y_qkv, 1, N, H, D, stream=stream)
+        if events:
+            events[1].record(stream)
+        kda.kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD, g,
+                              beta, o, 1, N, H, D, D, chunk=C, final_state=sT, stream=stream)
+        if events:
+            events[2].record(stream)
+        kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
+        if events:
+            events[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = {"conv": 0.0, "chunk": 0.0, "norm": 0.0}
+    for e in ev:
+        k_ms["conv"] += e[0].elapsed_time(e[1]) / args.steps
+        k_ms["chunk"] += e[1].elapsed_time(e[2]) / args.steps
+        k_ms["norm"] += e[2].elapsed_time(e[3]) / args.steps
+    log(f"timed prefill: {ms_step:.3f} ms/step; kernels {k_ms}")
+
+    nbytes = prefill_bytes(N, H, D, 1)
+    achieved = nbytes["chunk"] / (k_ms["chunk"] * 1e-3) / 1e9
+    flops = chunk_flops(N, H, D, C)
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded device-drawn inputs with the pages' layer shape and value "
+                "distributions (no dataset or weights involved)",
+        "config": {"workload": "prefill_T65536_H96_D128_bf16: conv+SiLU+L2 -> chunked gated "
+                               "delta rule -> gated RMSNorm",
+                   "T": N, "H": H, "D": D, "chunk": C, "sequences": 1, "state": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_kernel (kda_chunk_prefill)",
+                     "algorithmic_bytes_per_launch": nbytes["chunk"],
+                     "avg_launch_ms": k_ms["chunk"],
+                     "mfma_tflops_algorithmic": flops / (k_ms["chunk"] * 1e-3) / 1e12,
+                     "mfma_frac": flops / (k_ms["chunk"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "kernels_ms": k_ms,
+        "pipeline_gbs": sum(nbytes.values()) / (ms_step * 1e-3) / 1e9,
+    }
+
+    if not args.no_decode:
+        dspec = synth.CONFIGS[4]
+        B, Hd, Dd = dspec.B, dspec.H, dspec.D
+        steps = args.decode_steps
+        log(f"drawing inputs for {dspec.name}")
+        d = synth.decode_inputs(dspec, device="cuda", steps=steps)
+        od = torch.empty((B, Hd, Dd), dtype=d["x"].dtype, device="cuda")
+
+        def decode_pass(cs, S, events=None):
+            for t in range(steps):
+                if events:
+                    events[t][0].record(stream)
+                kda.kda_decode_step(d["x"][t], d["conv_w"], cs, d["g"][t], d["beta"][t], S, od,
+                                    B, Hd, Dd, stream=stream)
+                if events:
+                    events[t][1].record(stream)
+
+        decode_pass(d["conv_state"].clone(), d["S0"].clone())    # warm-up on copies
+        torch.cuda.synchronize()
+        dev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        cs, S = d["conv_state"].clone(), d["S0"].clone()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        decode_pass(cs, S, dev)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per = sorted(e[0].elapsed_time(e[1]) for e in dev)
+        med = per[len(per) // 2]
+        db = decode_bytes(B, Hd, Dd)
+        result["decode"] = {"workload": dspec.name, "B": B, "steps": steps,
+                            "ms_per_step_median": med, "ms_per_step_min": per[0],
+                            "ms_per_step_max": per[-1],
+                            "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
+                            "bytes_per_step": db, "TBps": db / (med * 1e-3) / 1e12,
+                            "tokens_per_s": B / (med * 1e-3),
+                            "hbm_frac": db / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"decode: {med:.3f} ms/step, {result['decode']['TBps']:.2f} TB/s")
+        del d, cs, S
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_tokens)
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

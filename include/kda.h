@@ -1,0 +1,162 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA token-mixer library, libkda.so.
+ *
+ * Kimi Delta Attention as drawn on "Inside Kimi K3" (lei.chat): the KDA
+ * one-head diagram (projections into 96 heads of 128 dims, Swish and L2 norm of
+ * q and k, channel-wise retention alpha and write strength beta with the
+ * log-decay bounded below by -5, a recurrent state updated by a decay and a
+ * delta-rule correction and evaluated chunkwise, the read S_t^T q_t, head
+ * RMSNorm and a full-rank sigmoid gate) and the KDA short-convolution diagram
+ * (a causal width-4 depthwise filter per channel, SiLU, the rolling state of the
+ * 3 previous raw inputs per channel of the combined QKV).  The state update is
+ * the one in the local-memory panel of "Animated Kimi K3 architecture diagram"
+ * (github.io): decay S with Diag(alpha_t), probe it with k_t, correct with
+ * e_t = v_t - Sbar_t^T k_t and write beta_t k_t e_t^T.
+ *
+ * Common rules for every entry point
+ * ----------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *   allocates no device memory and keeps no state besides a thread-local error
+ *   string.
+ * - Every call is asynchronous on the caller's stream `s` (0 = null stream) and
+ *   returns an int status; the message of the last failure on the calling
+ *   thread is kda_last_error().  No C++ exception crosses the ABI.
+ * - Arguments are checked on the host before anything is launched; a failed
+ *   check launches nothing and returns KDA_ERR_INVALID_ARG or
+ *   KDA_ERR_UNSUPPORTED.  KDA_ERR_HIP reports a launch failure.
+ * - `dtype` (KDA_F32 or KDA_BF16) is the element type of every per-token
+ *   tensor (x, y, q, k, v, g, beta, gate, o, conv states).  Recurrent states
+ *   are always fp32; conv filter weights and RMSNorm weights are always fp32.
+ *   Arithmetic is fp32 on the GPU in both modes; bf16 values are rounded to
+ *   nearest-even when stored.
+ * - Pointers to per-token tensors must be 16-byte aligned; token strides are
+ *   in elements and must be multiples of 8.
+ * - Results are deterministic: no atomics, fixed reduction orders.
+ * - Packed variable-length batches: when `cu_seqlens` (device int32
+ *   [num_seqs + 1], cu_seqlens[0] = 0, non-decreasing) is non-null, B must be
+ *   1 and T must equal cu_seqlens[num_seqs]; sequence i occupies tokens
+ *   [cu_seqlens[i], cu_seqlens[i+1]).  When it is null, there are B sequences
+ *   of T tokens each (num_seqs is ignored and taken as B).  The offsets live
+ *   in device memory and are not read on the host.
+ * - Shapes: H >= 1 heads; head sizes D, DK, DV in {64, 128}.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, forbidden alias */
+    KDA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    KDA_ERR_HIP = 3          /* a kernel launch failed */
+};
+
+enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 };
+
+/* Library version, e.g. 100 for 1.0.0. */
+int kda_version(void);
+
+/* Message describing the last non-zero status returned on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* kda_last_error(void);
+
+/*
+ * kda_conv -- short causal convolution + SiLU over projected q|k|v, then L2
+ * normalisation of q and k per (token, head).
+ * ("Inside Kimi K3", KDA short-convolution diagram; KDA one-head diagram.)
+ *
+ *   x              [B*T, 3*H*D]  projected inputs, token-major; channel index
+ *                                part*H*D + h*D + d with part 0 = q, 1 = k, 2 = v
+ *   w              [3*H*D, 4]    fp32 filter banks (q bank, k bank, v bank);
+ *                                tap 0 multiplies x_{t-3}, tap 3 multiplies x_t
+ *   y              [B*T, 3*H*D]  output: SiLU(conv) for all three parts, then
+ *                                q and k divided by sqrt(sum_d u_d^2 + l2_eps)
+ *   conv_state_in  [num_seqs, 3*H*D, 3] or NULL: raw inputs preceding each
+ *                                sequence, oldest first (NULL = zeros)
+ *   conv_state_out [num_seqs, 3*H*D, 3] or NULL: the last 3 raw inputs of each
+ *                                sequence's window (from conv_state_in where a
+ *                                sequence is shorter than 3); may equal
+ *                                conv_state_in (updated in place)
+ *   l2_eps         > 0, added under the square root (1e-6 in the tests)
+ * The sequence length is preserved and channels never mix; windows never
+ * cross sequence boundaries.  y must not overlap x.
+ */
+int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
+             void* conv_state_out, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+             int32_t T, int32_t H, int32_t D, int32_t dtype, float l2_eps, hipStream_t s);
+
+/*
+ * kda_chunk_prefill -- the gated delta rule over whole sequences, evaluated
+ * chunkwise: parallel within a chunk of `chunk` tokens, recurrent across
+ * chunks.  ("Inside Kimi K3", KDA one-head diagram; "Animated Kimi K3
+ * architecture diagram", local-memory panel.)  Per head and token t:
+ *   Sbar = Diag(exp(g_t)) S_{t-1};  e = v_t - Sbar^T k_t;
+ *   S_t = Sbar + beta_t k_t e^T;    o_t = S_t^T q_t.
+ *
+ *   q, k           [B*T, *] rows of H*DK elements at token stride
+ *                  qkv_token_stride (pass 3*H*DK to read kda_conv's y in place,
+ *                  or H*DK for separate tensors); q and k L2-normalised by the
+ *                  caller (kda_conv does it)
+ *   v              [B*T, *] rows of H*DV elements, same token stride
+ *   g              [B*T, H, DK] log-decay, precondition -5 <= g <= 0; both this
+ *                  kernel and the CPU oracle clamp it to [-5, 0]
+ *   beta           [B*T, H] write strength in (0, 1), already activated
+ *   o              [B*T, H, DV] output
+ *   initial_state  [num_seqs, H, DK, DV] fp32 or NULL (zeros)
+ *   final_state    [num_seqs, H, DK, DV] fp32 or NULL (not written); may equal
+ *                  initial_state (updated in place)
+ *   chunk          tokens per chunk: 32 or 64 (bf16); 16, 32 or 64 (fp32, where
+ *                  DK = 128 allows at most 32); the result does not depend on
+ *                  it beyond rounding
+ * o must not overlap any input.  Unsupported (dtype, DK, DV, chunk)
+ * combinations return KDA_ERR_UNSUPPORTED.
+ */
+int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_token_stride,
+                      const void* g, const void* beta, void* o, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t B, int32_t T, int32_t H, int32_t DK, int32_t DV, int32_t chunk,
+                      int32_t dtype, hipStream_t s);
+
+/*
+ * kda_decode_step -- one new token for each of B sequences: the conv window
+ * [conv_state (3 values), x_t] per channel, SiLU, L2 of q and k, then one
+ * gated-delta-rule step.  ("Inside Kimi K3", KDA short-convolution diagram,
+ * autoregressive rolling state; KDA one-head diagram.)
+ *
+ *   x           [B, 3*H*D]     projected new token (before the conv)
+ *   w           [3*H*D, 4]     fp32 filter banks, as in kda_conv
+ *   conv_state  [B, 3*H*D, 3]  rolling raw inputs, oldest first; updated in
+ *                              place to [x_{t-2}, x_{t-1}, x_t]
+ *   g           [B, H, D]      log-decay (clamped to [-5, 0]); beta [B, H]
+ *   state       [B, H, D, D]   fp32 recurrent state, updated in place
+ *   o           [B, H, D]      output S_t^T q_t; must not overlap any input
+ */
+int kda_decode_step(const void* x, const float* w, void* conv_state, const void* g,
+                    const void* beta, float* state, void* o, int32_t B, int32_t H, int32_t D,
+                    int32_t dtype, float l2_eps, hipStream_t s);
+
+/*
+ * kda_gated_norm -- head RMSNorm times a full-rank sigmoid gate.
+ * ("Inside Kimi K3", KDA one-head diagram: head RMSNorm and sigmoid gate.)
+ *   y[t,h,d] = o[t,h,d] / sqrt(mean_d o[t,h,d]^2 + eps) * weight[d]
+ *              * sigmoid(gate[t,h,d])
+ *   o, gate, y  [n_tokens, H, D]; gate holds pre-sigmoid logits
+ *   weight      [D] fp32, shared by all heads
+ * y may equal o (in place); otherwise it must not overlap the inputs.
+ */
+int kda_gated_norm(const void* o, const void* gate, const float* weight, void* y,
+                   int64_t n_tokens, int32_t H, int32_t D, float eps, int32_t dtype,
+                   hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

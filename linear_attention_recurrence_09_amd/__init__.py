@@ -1,0 +1,175 @@
+"""Python binding of libkda.so, the gfx950 KDA token-mixer library.
+
+Argument marshalling only: every function forwards tensor data pointers,
+sizes and torch's current HIP stream to the C ABI of the same name
+(``include/kda.h``) and raises :class:`KdaError` on a non-zero status.  All
+compute happens in the HIP kernels; there is no fallback path.  Outputs are
+allocated by the caller, as in the C ABI.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
+           "kda_decode_step", "kda_gated_norm", "kda_prefill", "KDA_F32", "KDA_BF16"]
+
+KDA_F32, KDA_BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+_DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libkda.so (built by ``python -m linear_attention_recurrence_09_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m linear_attention_recurrence_09_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.kda_version.restype = ctypes.c_int
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_conv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f, vp]
+        L.kda_chunk_prefill.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                        i32, i32, i32, i32, i32, vp]
+        L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f, vp]
+        L.kda_gated_norm.argtypes = [vp, vp, vp, vp, i64, i32, i32, f, i32, vp]
+        for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def kda_version() -> int:
+    return lib().kda_version()
+
+
+def kda_last_error() -> str:
+    return lib().kda_last_error().decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor, got {type(t)}")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(t):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise KdaError(fn, rc, kda_last_error())
+
+
+def _same_dtype(ref, *ts):
+    for t in ts:
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError("per-token tensors must share one dtype")
+
+
+def _f32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("weights and recurrent states must be float32")
+
+
+def kda_conv(x, w, y, B, T, H, D, conv_state_in=None, conv_state_out=None, cu_seqlens=None,
+             num_seqs=0, l2_eps=1e-6, stream=None):
+    """Short conv + SiLU over q|k|v, then L2 of q and k (see kda_conv in kda.h)."""
+    _same_dtype(x, y, conv_state_in, conv_state_out)
+    _f32(w)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check("kda_conv", lib().kda_conv(_ptr(x), _ptr(w), _ptr(y), _ptr(conv_state_in),
+                                      _ptr(conv_state_out), _ptr(cu_seqlens), num_seqs, B, T, H,
+                                      D, _dtype(x), l2_eps, _stream(stream)))
+
+
+def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, chunk=64,
+                      initial_state=None, final_state=None, cu_seqlens=None, num_seqs=0,
+                      stream=None):
+    """Chunkwise gated delta rule (see kda_chunk_prefill in kda.h).
+
+    q, k, v may be views into one [N, 3*H*D] tensor (kda_conv's output); they
+    are passed as data pointers with the given token stride.
+    """
+    _same_dtype(g, beta, o)
+    _f32(initial_state, final_state)
+    for t in (q, k, v):
+        if t.dtype != g.dtype or not t.is_cuda:
+            raise TypeError("q, k, v must be GPU tensors of the per-token dtype")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check("kda_chunk_prefill",
+           lib().kda_chunk_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), qkv_token_stride,
+                                   _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
+                                   _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, T, H, DK,
+                                   DV, chunk, _dtype(g), _stream(stream)))
+
+
+def kda_decode_step(x, w, conv_state, g, beta, state, o, B, H, D, l2_eps=1e-6, stream=None):
+    """One decode step; conv_state and state are updated in place."""
+    _same_dtype(x, conv_state, g, beta, o)
+    _f32(w, state)
+    _check("kda_decode_step",
+           lib().kda_decode_step(_ptr(x), _ptr(w), _ptr(conv_state), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(o), B, H, D, _dtype(x), l2_eps,
+                                 _stream(stream)))
+
+
+def kda_gated_norm(o, gate, weight, y, n_tokens, H, D, eps=1e-6, stream=None):
+    """Head RMSNorm times sigmoid(gate); y may be o itself."""
+    _same_dtype(o, gate, y)
+    _f32(weight)
+    _check("kda_gated_norm",
+           lib().kda_gated_norm(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), n_tokens, H, D, eps,
+                                _dtype(o), _stream(stream)))
+
+
+def kda_prefill(x, w, g, beta, gate, norm_w, H, D, cu_seqlens=None, num_seqs=1, B=1, T=None,
+                conv_state_in=None, conv_state_out=None, initial_state=None, final_state=None,
+                chunk=64, l2_eps=1e-6, rms_eps=1e-6, stream=None):
+    """The whole prefill path as three C ABI calls on one stream:
+    kda_conv -> kda_chunk_prefill (reading q, k, v in place from the conv
+    output) -> kda_gated_norm.  Returns (y_qkv, o, y)."""
+    N = x.shape[0]
+    if T is None:
+        T = N if cu_seqlens is not None else N // B
+    HD = H * D
+    y_qkv = torch.empty_like(x)
+    kda_conv(x, w, y_qkv, B, T, H, D, conv_state_in=conv_state_in,
+             conv_state_out=conv_state_out, cu_seqlens=cu_seqlens, num_seqs=num_seqs,
+             l2_eps=l2_eps, stream=stream)
+    o = torch.empty((N, H, D), dtype=x.dtype, device=x.device)
+    kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD, g, beta, o,
+                      B, T, H, D, D, chunk=chunk, initial_state=initial_state,
+                      final_state=final_state, cu_seqlens=cu_seqlens, num_seqs=num_seqs,
+                      stream=stream)
+    y = torch.empty_like(o)
+    kda_gated_norm(o, gate, norm_w, y, N, H, D, eps=rms_eps, stream=stream)
+    return y_qkv, o, y

@@ -1,0 +1,214 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: host-side argument
+// checks, then one or two kernel launches on the caller's stream.
+#include "kda.h"
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    return KDA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) intersect (byte ranges)
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int64_t esize(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == KDA_F32 || dtype == KDA_BF16; }
+bool valid_head(int d) { return d == 64 || d == 128; }
+
+// Resolve (cu_seqlens, num_seqs, B, T) into the sequence count and total tokens.
+int seq_layout(const char* fn, const int32_t* cu, int32_t num_seqs, int32_t B, int32_t T,
+               int* n_seqs, int64_t* n_tok) {
+    if (T < 0) return fail(KDA_ERR_INVALID_ARG, "%s: T must be >= 0 (got %d)", fn, T);
+    if (cu != nullptr) {
+        if (B != 1) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens requires B == 1 (got %d)", fn, B);
+        if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "%s: num_seqs must be >= 0", fn);
+        if (num_seqs == 0 && T > 0)
+            return fail(KDA_ERR_INVALID_ARG, "%s: T > 0 tokens but num_seqs == 0", fn);
+        *n_seqs = num_seqs;
+        *n_tok = T;
+    } else {
+        if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+        *n_seqs = B;
+        *n_tok = (int64_t)B * T;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
+             void* conv_state_out, const int32_t* cu_seqlens, int32_t num_seqs, int32_t B,
+             int32_t T, int32_t H, int32_t D, int32_t dtype, float l2_eps, hipStream_t s) {
+    const char* fn = "kda_conv";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be > 0", fn);
+    if (x == nullptr || w == nullptr || y == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, w and y must be non-null", fn);
+    int ns;
+    int64_t N;
+    if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    const int64_t P = 3LL * H * D;
+    const int64_t es = esize(dtype);
+    if (!aligned16(x) || !aligned16(y) || !aligned16(conv_state_in) || !aligned16(conv_state_out))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if (overlap(x, N * P * es, y, N * P * es))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y must not overlap x", fn);
+    const int64_t sbytes = (int64_t)ns * P * 3 * es;
+    if (conv_state_out != nullptr) {
+        if (conv_state_out != conv_state_in && overlap(conv_state_in, sbytes, conv_state_out, sbytes))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out partially overlaps conv_state_in", fn);
+        if (overlap(conv_state_out, sbytes, x, N * P * es) || overlap(conv_state_out, sbytes, y, N * P * es))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out overlaps x or y", fn);
+    }
+    if (N == 0 && (conv_state_out == nullptr || ns == 0)) return ok();
+    return hip_status(kda::launch_conv(x, w, y, conv_state_in, conv_state_out, cu_seqlens, ns,
+                                       T, N, H, D, dtype, l2_eps, s),
+                      fn);
+}
+
+int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_token_stride,
+                      const void* g, const void* beta, void* o, const float* initial_state,
+                      float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t B, int32_t T, int32_t H, int32_t DK, int32_t DV, int32_t chunk,
+                      int32_t dtype, hipStream_t s) {
+    const char* fn = "kda_chunk_prefill";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (!valid_head(DK) || !valid_head(DV))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: DK and DV must be 64 or 128 (got %d, %d)", fn, DK, DV);
+    if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || beta == nullptr || o == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: q, k, v, g, beta and o must be non-null", fn);
+    const int64_t row = (int64_t)H * (DK > DV ? DK : DV);
+    if (qkv_token_stride < row || qkv_token_stride % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "%s: qkv_token_stride must be >= H*max(DK,DV) and a multiple of 8 (got %lld)",
+                    fn, (long long)qkv_token_stride);
+    int ns;
+    int64_t N;
+    if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    const kda::ChunkPlan plan = kda::plan_chunk(dtype, DK, DV, chunk, (int64_t)ns * H);
+    if (!plan.ok)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: no variant for dtype=%d DK=%d DV=%d chunk=%d", fn,
+                    dtype, DK, DV, chunk);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if ((int64_t)ns * H * (DV / plan.dvs) > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", fn);
+    const int64_t es = esize(dtype);
+    const int64_t qkv_bytes = N > 0 ? ((N - 1) * qkv_token_stride + row) * es : 0;
+    const int64_t o_bytes = N * H * DV * es;
+    if (overlap(o, o_bytes, q, qkv_bytes) || overlap(o, o_bytes, k, qkv_bytes) ||
+        overlap(o, o_bytes, v, qkv_bytes) || overlap(o, o_bytes, g, N * H * DK * es) ||
+        overlap(o, o_bytes, beta, N * H * es))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not overlap an input", fn);
+    const int64_t st_bytes = (int64_t)ns * H * DK * DV * 4;
+    if (final_state != nullptr) {
+        if ((const void*)final_state != (const void*)initial_state &&
+            overlap(final_state, st_bytes, initial_state, st_bytes))
+            return fail(KDA_ERR_INVALID_ARG, "%s: final_state partially overlaps initial_state", fn);
+        if (overlap(final_state, st_bytes, o, o_bytes))
+            return fail(KDA_ERR_INVALID_ARG, "%s: final_state overlaps o", fn);
+    }
+    if (ns == 0) return ok();
+    return hip_status(kda::launch_chunk(plan, q, k, v, qkv_token_stride, g, beta, o,
+                                        initial_state, final_state, cu_seqlens, ns, T, H, DK,
+                                        DV, dtype, s),
+                      fn);
+}
+
+int kda_decode_step(const void* x, const float* w, void* conv_state, const void* g,
+                    const void* beta, float* state, void* o, int32_t B, int32_t H, int32_t D,
+                    int32_t dtype, float l2_eps, hipStream_t s) {
+    const char* fn = "kda_decode_step";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be > 0", fn);
+    if (x == nullptr || w == nullptr || conv_state == nullptr || g == nullptr || beta == nullptr ||
+        state == nullptr || o == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: every pointer must be non-null", fn);
+    if (!aligned16(x) || !aligned16(conv_state) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if ((int64_t)B * H > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", fn);
+    const int64_t es = esize(dtype);
+    const int64_t P = 3LL * H * D;
+    const int64_t o_bytes = (int64_t)B * H * D * es;
+    if (overlap(o, o_bytes, x, B * P * es) || overlap(o, o_bytes, conv_state, B * P * 3 * es) ||
+        overlap(o, o_bytes, g, (int64_t)B * H * D * es) || overlap(o, o_bytes, beta, (int64_t)B * H * es) ||
+        overlap(o, o_bytes, state, (int64_t)B * H * D * D * 4))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not overlap an input", fn);
+    if (overlap(state, (int64_t)B * H * D * D * 4, conv_state, B * P * 3 * es))
+        return fail(KDA_ERR_INVALID_ARG, "%s: state overlaps conv_state", fn);
+    if (B == 0) return ok();
+    return hip_status(kda::launch_decode(x, w, conv_state, g, beta, state, o, B, H, D, dtype,
+                                         l2_eps, s),
+                      fn);
+}
+
+int kda_gated_norm(const void* o, const void* gate, const float* weight, void* y,
+                   int64_t n_tokens, int32_t H, int32_t D, float eps, int32_t dtype,
+                   hipStream_t s) {
+    const char* fn = "kda_gated_norm";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (n_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "%s: n_tokens must be >= 0", fn);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: eps must be > 0", fn);
+    if (o == nullptr || gate == nullptr || weight == nullptr || y == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: o, gate, weight and y must be non-null", fn);
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(weight) || !aligned16(y))
+        return fail(KDA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    const int64_t rows = n_tokens * H;
+    const int64_t bytes = rows * D * esize(dtype);
+    if (y != o && overlap(y, bytes, o, bytes))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y partially overlaps o", fn);
+    if (overlap(y, bytes, gate, bytes))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y overlaps gate", fn);
+    if (rows == 0) return ok();
+    return hip_status(kda::launch_gated_norm(o, gate, weight, y, rows, D, eps, dtype, s), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// kda_conv.hip -- short causal depthwise convolution + SiLU over projected
+// q|k|v, then L2 normalisation of q and k per (token, head) (gfx950).
+//
+// "Inside Kimi K3" (lei.chat), KDA short-convolution diagram: each channel is
+// filtered on its own over a causal window of 4 tokens (taps w0..w3 on
+// x_{t-3}..x_t), SiLU follows, the length is kept by left padding, and the
+// rolling state of a sequence is its last 3 raw inputs per channel.  KDA
+// one-head diagram: q and k are then L2-normalised over the 128-d head.
+//
+// HBM-bound stencil: read x once (plus a 3-token halo per tile) and write y
+// once.  A thread owns 8 consecutive channels (one 16-byte bf16 vector) for a
+// tile of kTile tokens and slides the 3-value window in registers; D/8 lanes
+// of one head reduce the sum of squares with xor shuffles.  A block covers
+// 2048 channels; windows restart at every sequence start.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvChannels = kConvThreads * 8;
+constexpr int kTile = 32;
+
+struct SeqRange {
+    int s;
+    int64_t start, end;
+};
+
+// Sequence holding token t: the largest s with start(s) <= t (empty
+// sequences are skipped because their successor starts at the same token).
+__device__ __forceinline__ SeqRange find_seq(const int32_t* cu, int num_seqs, int T, int64_t t) {
+    SeqRange r;
+    if (cu == nullptr) {
+        r.s = (int)(t / T);
+        r.start = (int64_t)r.s * T;
+        r.end = r.start + T;
+        return r;
+    }
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    r.s = lo;
+    r.start = cu[lo];
+    r.end = cu[lo + 1];
+    return r;
+}
+
+// a[i] for a runtime i in [0, 3) without indexing registers dynamically
+__device__ __forceinline__ float pick3(const float a[3], int i) {
+    return i == 0 ? a[0] : (i == 1 ? a[1] : a[2]);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_state8(const T* state_in, int64_t s, int P, int c0,
+                                            float st[8][3]) {
+    if (state_in == nullptr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st[e][0] = st[e][1] = st[e][2] = 0.f;
+        return;
+    }
+    // 8 channels x 3 slots = 24 contiguous values
+    const T* p = state_in + (s * P + c0) * 3;
+    float v[24];
+    load8(p, v);
+    load8(p + 8, v + 8);
+    load8(p + 16, v + 16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        st[e][0] = v[3 * e + 0];
+        st[e][1] = v[3 * e + 1];
+        st[e][2] = v[3 * e + 2];
+    }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kConvThreads)
+conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ y,
+            const T* __restrict__ state_in, const int32_t* __restrict__ cu, int num_seqs,
+            int T_len, int64_t N, int P, int HD, float l2_eps) {
+    const int c0 = blockIdx.y * kConvChannels + threadIdx.x * 8;
+    const bool active = c0 < P;
+    const int64_t t0 = (int64_t)blockIdx.x * kTile;
+    const int64_t t1 = t0 + kTile < N ? t0 + kTile : N;
+    const bool is_qk = c0 < 2 * HD;   // uniform over the D/8 lanes of a head
+
+    float wt[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wt[e][i] = active ? w[(c0 + e) * 4 + i] : 0.f;
+
+    SeqRange sr = find_seq(cu, num_seqs, T_len, t0);
+    // window: win[e][0] = x_{t-3}, win[e][1] = x_{t-2}, win[e][2] = x_{t-1}
+    float win[8][3];
+    if (active) {
+        float st[8][3];
+        load_state8(state_in, sr.s, P, c0, st);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int64_t tau = t0 - 3 + j;
+            if (tau >= sr.start) {
+                float xv[8];
+                load8(x + tau * P + c0, xv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[e][j] = xv[e];
+            } else {
+                const int slot = (int)(tau - sr.start) + 3;   // in [0, 3)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[e][j] = pick3(st[e], slot);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) win[e][0] = win[e][1] = win[e][2] = 0.f;
+    }
+
+    for (int64_t t = t0; t < t1; ++t) {
+        if (t >= sr.end) {               // a new sequence starts at t
+            do {
+                if (cu == nullptr) {
+                    sr.s += 1;
+                    sr.start = sr.end;
+                    sr.end = sr.start + T_len;
+                } else if (sr.s + 1 < num_seqs) {
+                    sr.s += 1;
+                    sr.start = cu[sr.s];
+                    sr.end = cu[sr.s + 1];
+                } else {
+                    sr.end = t1;         // offsets inconsistent with N: stay in bounds
+                }
+            } while (t >= sr.end);
+            if (active) load_state8(state_in, sr.s, P, c0, win);
+        }
+        float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (active) load8(x + t * P + c0, xv);
+        float out[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pre = wt[e][0] * win[e][0] + wt[e][1] * win[e][1] +
+                              wt[e][2] * win[e][2] + wt[e][3] * xv[e];
+            out[e] = siluf_(pre);
+            ss += out[e] * out[e];
+            win[e][0] = win[e][1];
+            win[e][1] = win[e][2];
+            win[e][2] = xv[e];
+        }
+        ss = group_sum<D / 8>(ss);
+        if (is_qk) {
+            const float inv = rsqrt_nr(ss + l2_eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] *= inv;
+        }
+        if (active) store8(y + t * P + c0, out);
+    }
+}
+
+// Rolling state after each sequence: its last 3 raw inputs, taken from the
+// incoming state where the sequence is shorter than 3.  Each thread reads its
+// own state slots before writing them, so state_out may equal state_in.
+template <typename T>
+__global__ void __launch_bounds__(kConvThreads)
+conv_state_kernel(const T* __restrict__ x, const T* state_in, T* state_out,
+                  const int32_t* __restrict__ cu, int T_len, int P) {
+    const int s = blockIdx.x;
+    const int c0 = blockIdx.y * kConvChannels + threadIdx.x * 8;
+    if (c0 >= P) return;
+    const int64_t start = cu ? (int64_t)cu[s] : (int64_t)s * T_len;
+    const int64_t len = cu ? (int64_t)cu[s + 1] - start : (int64_t)T_len;
+    float st[8][3];
+    load_state8(state_in, s, P, c0, st);
+    float v[24];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int64_t tau = len - 3 + j;
+        if (tau >= 0) {
+            float xv[8];
+            load8(x + (start + tau) * P + c0, xv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[3 * e + j] = xv[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[3 * e + j] = pick3(st[e], (int)(tau + 3));
+        }
+    }
+    T* p = state_out + ((int64_t)s * P + c0) * 3;
+    store8(p, v);
+    store8(p + 8, v + 8);
+    store8(p + 16, v + 16);
+}
+
+template <typename T, int D>
+hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* state_in,
+                         void* state_out, const int32_t* cu, int num_seqs, int T_len,
+                         int64_t N, int H, float l2_eps, hipStream_t s) {
+    const int P = 3 * H * D;
+    const unsigned cblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
+    if (N > 0) {
+        const unsigned tiles = (unsigned)((N + kTile - 1) / kTile);
+        hipLaunchKernelGGL((conv_kernel<T, D>), dim3(tiles, cblocks), dim3(kConvThreads), 0, s,
+                           (const T*)x, w, (T*)y, (const T*)state_in, cu, num_seqs, T_len, N, P,
+                           H * D, l2_eps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (state_out != nullptr && num_seqs > 0) {
+        hipLaunchKernelGGL((conv_state_kernel<T>), dim3((unsigned)num_seqs, cblocks),
+                           dim3(kConvThreads), 0, s, (const T*)x, (const T*)state_in,
+                           (T*)state_out, cu, T_len, P);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_conv(const void* x, const float* w, void* y, const void* state_in,
+                       void* state_out, const int32_t* cu, int num_seqs, int T, int64_t N,
+                       int H, int D, int dtype, float l2_eps, hipStream_t s) {
+    if (dtype == 0) {
+        return D == 64 ? launch_conv_t<float, 64>(x, w, y, state_in, state_out, cu, num_seqs, T,
+                                                  N, H, l2_eps, s)
+                       : launch_conv_t<float, 128>(x, w, y, state_in, state_out, cu, num_seqs,
+                                                   T, N, H, l2_eps, s);
+    }
+    return D == 64 ? launch_conv_t<__bf16, 64>(x, w, y, state_in, state_out, cu, num_seqs, T, N,
+                                               H, l2_eps, s)
+                   : launch_conv_t<__bf16, 128>(x, w, y, state_in, state_out, cu, num_seqs, T,
+                                                N, H, l2_eps, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,186 @@
+// kda_decode.hip -- one decode step of the KDA mixer for B sequences (gfx950).
+//
+// "Inside Kimi K3" (lei.chat), KDA short-convolution diagram: autoregressive
+// decoding keeps the 3 previous raw inputs of every channel of the combined
+// QKV; the new window is [state, x_t].  KDA one-head diagram and "Animated
+// Kimi K3 architecture diagram" (github.io), local-memory panel: decay the
+// key rows of S, probe with k, correct e = v - Sbar^T k, write beta k e^T,
+// read S^T q.
+//
+// One workgroup per (sequence, head).  The state is one streaming pass: each
+// thread loads its 16 (D = 128) float4's of S, decays them, accumulates
+// Sbar^T k and Sbar^T q for its 4 columns, the column sums are reduced across
+// row groups, and the same registers are updated and stored.  The read uses
+// o = Sbar^T q + beta (k . q) e, which equals S_t^T q.  HBM traffic is one read
+// and one write of the fp32 state plus the small per-token tensors.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kDecThreads = 256;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecThreads)
+decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_state,
+              const T* __restrict__ g, const T* __restrict__ beta, float* state,
+              T* __restrict__ o, int H, float l2_eps) {
+    constexpr int CG = D / 4;                 // float4 column groups per row
+    constexpr int R = kDecThreads / CG;       // row groups
+    constexpr int RPT = D / R;                // rows per thread
+    constexpr int CT = 3 * D / 2;             // conv threads (2 channels each)
+    __shared__ float su[3 * D];               // conv output: q | k | v of this head
+    __shared__ float sa[D];                   // per-key-channel retention
+    __shared__ float sred[kDecThreads / 64][CG][8];
+    __shared__ float skq;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int h = bh % H;
+    const int P = 3 * H * D;
+
+    // ---- state loads first: the longest-latency traffic ---------------------
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    float* Sbh = state + (int64_t)bh * D * D;
+    float4 sv[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        sv[j] = *reinterpret_cast<const float4*>(Sbh + (rg + R * j) * D + 4 * cg);
+
+    // ---- conv window + SiLU + L2 -------------------------------------------
+    float y0 = 0.f, y1 = 0.f;
+    int part = 3;
+    if (tid < CT) {
+        const int cc = 2 * tid;               // channel within [q | k | v] of head h
+        part = cc / D;
+        const int d = cc % D;
+        const int c = part * H * D + h * D + d;
+        float x0, x1;
+        load2(x + (int64_t)b * P + c, x0, x1);
+        T* sp = conv_state + ((int64_t)b * P + c) * 3;
+        float s00, s01, s02, s10, s11, s12;
+        load2(sp, s00, s01);
+        load2(sp + 2, s02, s10);
+        load2(sp + 4, s11, s12);
+        const float* wc = w + c * 4;
+        const float p0 = wc[0] * s00 + wc[1] * s01 + wc[2] * s02 + wc[3] * x0;
+        const float p1 = wc[4] * s10 + wc[5] * s11 + wc[6] * s12 + wc[7] * x1;
+        y0 = siluf_(p0);
+        y1 = siluf_(p1);
+        store2(sp, s01, s02);
+        store2(sp + 2, x0, s11);
+        store2(sp + 4, s12, x1);
+    }
+    float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
+    if (part < 2) {
+        const float inv = rsqrt_nr(ss + l2_eps);
+        y0 *= inv;
+        y1 *= inv;
+    }
+    if (tid < CT) {
+        su[2 * tid] = y0;
+        su[2 * tid + 1] = y1;
+    }
+    if (tid < D) sa[tid] = fast_exp2(clamp_log_decay(to_f(g[(int64_t)bh * D + tid])) * kLog2e);
+    const float bt = to_f(beta[bh]);
+    __syncthreads();
+
+    if (wave == 0) {   // k . q
+        float kq = 0.f;
+        for (int i = lane; i < D; i += 64) kq += su[i] * su[D + i];
+        kq = group_sum<64>(kq);
+        if (lane == 0) skq = kq;
+    }
+
+    // ---- decay, and the column sums Sbar^T k, Sbar^T q ----------------------
+    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int i = rg + R * j;
+        const float a = sa[i];
+        sv[j].x *= a; sv[j].y *= a; sv[j].z *= a; sv[j].w *= a;
+        const float ki = su[D + i], qi = su[i];
+        ak.x += ki * sv[j].x; ak.y += ki * sv[j].y; ak.z += ki * sv[j].z; ak.w += ki * sv[j].w;
+        aq.x += qi * sv[j].x; aq.y += qi * sv[j].y; aq.z += qi * sv[j].z; aq.w += qi * sv[j].w;
+    }
+    // row groups inside a wave differ in lane bits >= log2(CG)
+#pragma unroll
+    for (int m = CG; m < 64; m <<= 1) {
+        ak.x += __shfl_xor(ak.x, m, 64); ak.y += __shfl_xor(ak.y, m, 64);
+        ak.z += __shfl_xor(ak.z, m, 64); ak.w += __shfl_xor(ak.w, m, 64);
+        aq.x += __shfl_xor(aq.x, m, 64); aq.y += __shfl_xor(aq.y, m, 64);
+        aq.z += __shfl_xor(aq.z, m, 64); aq.w += __shfl_xor(aq.w, m, 64);
+    }
+    if (lane < CG) {
+        float* r = sred[wave][cg];
+        r[0] = ak.x; r[1] = ak.y; r[2] = ak.z; r[3] = ak.w;
+        r[4] = aq.x; r[5] = aq.y; r[6] = aq.z; r[7] = aq.w;
+    }
+    __syncthreads();
+    float tk[4] = {0.f, 0.f, 0.f, 0.f}, tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int wv = 0; wv < kDecThreads / 64; ++wv)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tk[e] += sred[wv][cg][e];
+            tq[e] += sred[wv][cg][4 + e];
+        }
+    const float kq = skq;
+    float ev[4], ov[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ev[e] = su[2 * D + 4 * cg + e] - tk[e];
+        ov[e] = tq[e] + bt * kq * ev[e];
+    }
+    if (rg == 0) {
+        T* op = o + (int64_t)bh * D + 4 * cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) op[e] = from_f<T>(ov[e]);
+    }
+    // ---- write: S = Sbar + beta k e^T ---------------------------------------
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int i = rg + R * j;
+        const float bk = bt * su[D + i];
+        float4 r = sv[j];
+        r.x += bk * ev[0]; r.y += bk * ev[1]; r.z += bk * ev[2]; r.w += bk * ev[3];
+        *reinterpret_cast<float4*>(Sbh + i * D + 4 * cg) = r;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_t(const void* x, const float* w, void* conv_state, const void* g,
+                           const void* beta, float* state, void* o, int B, int H, float l2_eps,
+                           hipStream_t s) {
+    const int64_t blocks = (int64_t)B * H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)blocks), dim3(kDecThreads), 0, s,
+                       (const T*)x, w, (T*)conv_state, (const T*)g, (const T*)beta, state, (T*)o,
+                       H, l2_eps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const void* x, const float* w, void* conv_state, const void* g,
+                         const void* beta, float* state, void* o, int B, int H, int D,
+                         int dtype, float l2_eps, hipStream_t s) {
+    if (dtype == 0) {
+        return D == 64 ? launch_decode_t<float, 64>(x, w, conv_state, g, beta, state, o, B, H,
+                                                    l2_eps, s)
+                       : launch_decode_t<float, 128>(x, w, conv_state, g, beta, state, o, B, H,
+                                                     l2_eps, s);
+    }
+    return D == 64 ? launch_decode_t<__bf16, 64>(x, w, conv_state, g, beta, state, o, B, H,
+                                                 l2_eps, s)
+                   : launch_decode_t<__bf16, 128>(x, w, conv_state, g, beta, state, o, B, H,
+                                                  l2_eps, s);
+}
+
+}  // namespace kda

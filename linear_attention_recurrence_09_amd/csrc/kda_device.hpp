@@ -1,0 +1,138 @@
+// kda_device.hpp -- device helpers shared by the gfx950 KDA kernels.
+//
+// I/O element types: float (fp32 mode) and __bf16 (bf16 mode).  bf16 -> fp32 is
+// exact; fp32 -> bf16 uses the hardware round-to-nearest-even conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLogDecayMin = -5.0f;  // the pages bound the log-decay below by -5
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f(float x);
+template <>
+__device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f<__bf16>(float x) { return (__bf16)x; }
+
+// ---- 8-wide vector I/O (16 B for bf16, 2 x 16 B for fp32) -------------------
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const __bf16* p, float v[8]) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(__bf16* p, const float v[8]) {
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (__bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+// ---- 2-wide I/O --------------------------------------------------------------
+__device__ __forceinline__ void load2(const float* p, float& a, float& b) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    a = t.x; b = t.y;
+}
+__device__ __forceinline__ void load2(const __bf16* p, float& a, float& b) {
+    const bf16x2 t = *reinterpret_cast<const bf16x2*>(p);
+    a = (float)t[0]; b = (float)t[1];
+}
+__device__ __forceinline__ void store2(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+__device__ __forceinline__ void store2(__bf16* p, float a, float b) {
+    bf16x2 t;
+    t[0] = (__bf16)a; t[1] = (__bf16)b;
+    *reinterpret_cast<bf16x2*>(p) = t;
+}
+
+// ---- math --------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoidf_(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
+__device__ __forceinline__ float siluf_(float x) { return x * sigmoidf_(x); }
+__device__ __forceinline__ float clamp_log_decay(float g) {
+    return __builtin_amdgcn_fmed3f(g, kLogDecayMin, 0.0f);
+}
+// 1/sqrt(x) with one Newton step on top of the hardware estimate.
+__device__ __forceinline__ float rsqrt_nr(float x) {
+    float r = __builtin_amdgcn_rsqf(x);
+    return r * (1.5f - 0.5f * x * r * r);
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// ---- MFMA fragments (16 x 16 output tiles) -----------------------------------
+// A operand: lane l supplies row (l % 16) and KPL consecutive k's starting at
+// KPL * (l / 16); B operand symmetric with the column index; the 4 accumulator
+// values of lane l are rows 4 * (l / 16) + i, column l % 16.
+template <typename OpT>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+    static constexpr int KPL = 8;   // operand elements per lane
+    static constexpr int KI = 32;   // reduction depth per instruction
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag load(const __bf16* p) {
+        return *reinterpret_cast<const frag*>(p);
+    }
+    static __device__ __forceinline__ frag pack(const float v[8]) {
+        frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (__bf16)v[i];
+        return f;
+    }
+    static __device__ __forceinline__ void unpack(frag f, float v[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)f[i];
+    }
+};
+
+template <>
+struct Mma<float> {
+    static constexpr int KPL = 1;
+    static constexpr int KI = 4;
+    typedef float frag;
+    static __device__ __forceinline__ floatx4 mma(frag a, frag b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag load(const float* p) { return *p; }
+    static __device__ __forceinline__ frag pack(const float v[1]) { return v[0]; }
+    static __device__ __forceinline__ void unpack(frag f, float v[1]) { v[0] = f; }
+};
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace kda

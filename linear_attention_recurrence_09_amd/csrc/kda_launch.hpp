@@ -1,0 +1,34 @@
+// kda_launch.hpp -- host-side launchers of the gfx950 kernels (internal).
+// Arguments are validated by the C ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+hipError_t launch_gated_norm(const void* o, const void* gate, const float* w, void* y,
+                             int64_t rows, int D, float eps, int dtype, hipStream_t s);
+
+hipError_t launch_conv(const void* x, const float* w, void* y, const void* state_in,
+                       void* state_out, const int32_t* cu, int num_seqs, int T, int64_t N,
+                       int H, int D, int dtype, float l2_eps, hipStream_t s);
+
+hipError_t launch_decode(const void* x, const float* w, void* conv_state, const void* g,
+                         const void* beta, float* state, void* o, int B, int H, int D,
+                         int dtype, float l2_eps, hipStream_t s);
+
+// Chunked prefill configuration chosen on the host.
+struct ChunkPlan {
+    int nb;       // 16-token blocks per chunk (chunk = 16 * nb)
+    int dvs;      // value columns per workgroup (DV / dvs workgroups per head)
+    bool ok;      // false when no compiled variant fits the request
+};
+ChunkPlan plan_chunk(int dtype, int DK, int DV, int chunk, int64_t n_chains);
+
+hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, const void* v,
+                        int64_t stride, const void* g, const void* beta, void* o,
+                        const float* s0, float* sT, const int32_t* cu, int num_seqs, int T,
+                        int H, int DK, int DV, int dtype, hipStream_t s);
+
+}  // namespace kda

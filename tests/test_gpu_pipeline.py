@@ -1,0 +1,157 @@
+"""End-to-end parity of the prefill path (kda_conv -> kda_chunk_prefill ->
+kda_gated_norm) and of decode against the CPU oracle, at the five workloads'
+full sizes (the oracle checks sampled heads / sampled (sequence, head) pairs
+there), plus stress variants that expose the inter-chunk carry, a closed-form
+check that needs no oracle, determinism and out-of-bounds canaries."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_recurrence_09_amd as kda
+import synth
+from oracle import c_oracle
+from tests.kda_testlib import (TOL, compare_prefill, f64, gpu_heads, gpu_prefill, head_channels,
+                               oracle_prefill, rel_l2, report)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_config(spec, heads, prefix=None):
+    print(f"workload {spec.name} heads={heads} prefix={prefix}", flush=True)
+    inp = synth.prefill_inputs(spec, device="cuda")
+    out = gpu_prefill(inp, prefix=prefix)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(inp, heads, prefix=prefix)
+    return compare_prefill(gpu_heads(out, spec.H, spec.D, heads), ref, spec.dtype)
+
+
+def test_config0_tiny_fp32_all_heads():
+    _run_config(synth.CONFIGS[0], heads=[0, 1])
+
+
+def test_config1_T4096_sampled_heads():
+    _run_config(synth.CONFIGS[1], heads=[0, 37, 95])
+
+
+def test_config2_T65536_prefixes_and_snapshots():
+    """State carried over 1024 chunks, compared at T' = 1024, 8192, 65536:
+    three GPU calls on prefixes of one sequence against one oracle pass."""
+    spec = synth.CONFIGS[2]
+    heads = [5, 90]
+    print(f"workload {spec.name} heads={heads}", flush=True)
+    inp = synth.prefill_inputs(spec, device="cuda")
+    snaps = (1024, 8192, 65536)
+    ref = oracle_prefill(inp, heads, snap_t=snaps)
+    for i, tp in enumerate(snaps):
+        out = gpu_prefill(inp, prefix=tp)
+        got = gpu_heads(out, spec.H, spec.D, heads)
+        tol = TOL[spec.dtype]
+        assert report(f"o[:{tp}]", got["o"], ref["o"][:tp], tol) <= tol
+        assert report(f"y[:{tp}]", got["y"], ref["y"][:tp], tol) <= tol
+        assert report(f"S_{tp}", got["S_final"][0], ref["snaps"][0, i], tol) <= tol
+        del out
+
+
+def test_config3_varlen_sampled_heads():
+    _run_config(synth.CONFIGS[3], heads=[3, 64])
+
+
+def test_stress_slow_decay():
+    _run_config(synth.STRESS["slow_decay"], heads=[1, 50])
+
+
+def test_stress_long_carry_all_heads():
+    """~15% of the entering state survives 1024 chunks here, so a broken
+    carry or fp32 drift across chunks shows."""
+    _run_config(synth.STRESS["long_carry"], heads=[0, 1, 2, 3])
+
+
+def test_config4_decode_64_steps_sampled_pairs():
+    spec = synth.CONFIGS[4]
+    B, H, D, steps = spec.B, spec.H, spec.D, spec.steps
+    print(f"workload {spec.name}", flush=True)
+    d = synth.decode_inputs(spec, device="cuda")
+    cs = d["conv_state"].clone()
+    S = d["S0"].clone()
+    o = torch.empty((B, H, D), dtype=d["x"].dtype, device="cuda")
+    heads, bs = [0, 47, 95], [0, 100, 255]
+    cols = {h: torch.as_tensor(head_channels(H, D, [h]), device="cuda") for h in heads}
+    ref_cs = {h: f64(d["conv_state"][bs].index_select(1, cols[h])) for h in heads}
+    ref_S = {h: f64(d["S0"][bs][:, [h]]) for h in heads}
+    w = {h: f64(d["conv_w"].index_select(0, cols[h])) for h in heads}
+    tol = TOL[spec.dtype]
+    worst = 0.0
+    for t in range(steps):
+        kda.kda_decode_step(d["x"][t], d["conv_w"], cs, d["g"][t], d["beta"][t], S, o, B, H, D)
+        for h in heads:
+            o_ref, ref_cs[h], ref_S[h] = c_oracle.kda_decode_step(
+                f64(d["x"][t][bs].index_select(1, cols[h])), w[h], ref_cs[h],
+                f64(d["g"][t][bs][:, [h]]), f64(d["beta"][t][bs][:, [h]]), ref_S[h], 1, D)
+            r = rel_l2(f64(o[bs][:, [h]]), o_ref)
+            worst = max(worst, r)
+            assert r <= tol, (t, h, r)
+    print(f"  o (all 64 steps, sampled pairs): worst rel_l2={worst:.3e}", flush=True)
+    for h in heads:
+        assert report(f"S[h={h}]", f64(S[bs][:, [h]]), ref_S[h], tol) <= tol
+        assert np.array_equal(f64(cs[bs].index_select(1, cols[h])), ref_cs[h])
+
+
+def test_beta_one_reads_back_values_on_gpu():
+    """Closed form without the oracle: with beta = 1 the correction makes the
+    written key read back its value, so q_t = k_t gives o_t = v_t."""
+    H, D, N = 4, 128, 200
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    k = torch.randn((N, H, D), generator=gen, device="cuda")
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = torch.randn((N, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    g = (-5 * torch.rand((N, H, D), generator=gen, device="cuda")).to(torch.bfloat16)
+    beta = torch.ones((N, H), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(v)
+    kda.kda_chunk_prefill(k.reshape(N, H * D), k.reshape(N, H * D), v.reshape(N, H * D), H * D,
+                          g, beta, o, 1, N, H, D, D)
+    # k rounded to bf16 is unit-norm only to ~1e-3, which the read inherits
+    assert report("o vs v", f64(o), f64(v), 2e-2) <= 2e-2
+
+
+def test_deterministic_bitwise():
+    spec = synth.scaled(synth.CONFIGS[1], lengths=(1000,), H=8)
+    inp = synth.prefill_inputs(spec, device="cuda")
+    a = gpu_prefill(inp)
+    b = gpu_prefill(inp)
+    torch.cuda.synchronize()
+    for key in ("y_qkv", "o", "y", "S_final", "conv_state_out"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_outputs_stay_in_bounds():
+    """Guard bands around every output must be untouched."""
+    spec = synth.scaled(synth.CONFIGS[3], n_seqs=5, len_lo=1, len_hi=200, H=4)
+    inp = synth.prefill_inputs(spec, device="cuda")
+    H, D = spec.H, spec.D
+    N = inp["x"].shape[0]
+    S = len(inp["lengths"])
+    HD = H * D
+    pad = 4096
+    dt = inp["x"].dtype
+    cu = torch.tensor(inp["cu"], dtype=torch.int32, device="cuda")
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), 12345.0, dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n]
+
+    yb, y = guarded(N * 3 * HD, dt)
+    ob, o = guarded(N * HD, dt)
+    nb, yn = guarded(N * HD, dt)
+    sb, sT = guarded(S * H * D * D, torch.float32)
+    cb, cso = guarded(S * 3 * HD * 3, dt)
+    y2, o2, yn2 = y.view(N, 3 * HD), o.view(N, H, D), yn.view(N, H, D)
+    kda.kda_conv(inp["x"], inp["conv_w"], y2, 1, N, H, D, conv_state_out=cso.view(S, 3 * HD, 3),
+                 cu_seqlens=cu, num_seqs=S)
+    kda.kda_chunk_prefill(y2[:, :HD], y2[:, HD:2 * HD], y2[:, 2 * HD:], 3 * HD, inp["g"],
+                          inp["beta"], o2, 1, N, H, D, D, initial_state=inp["S0"],
+                          final_state=sT.view(S, H, D, D), cu_seqlens=cu, num_seqs=S)
+    kda.kda_gated_norm(o2, inp["gate"], inp["norm_w"], yn2, N, H, D)
+    torch.cuda.synchronize()
+    for name, buf in (("y_qkv", yb), ("o", ob), ("y", nb), ("S_final", sb), ("conv_state", cb)):
+        assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0), name
