@@ -35,6 +35,30 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
+// Optional stage timing (profiling builds define KDA_STAGE_PROFILE and the
+// array; workgroup 0, thread 0 records the cycles spent in each stage).
+#ifdef KDA_STAGE_PROFILE
+extern __device__ unsigned long long kda_stage_cycles[8];
+#define KDA_PROF_INIT()                                          \
+    unsigned long long prof_t_ = __builtin_readcyclecounter();  \
+    unsigned long long prof_acc_[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+#define KDA_PROF_MARK(i)                                                  \
+    do {                                                                  \
+        const unsigned long long t_ = __builtin_readcyclecounter();      \
+        prof_acc_[i] += t_ - prof_t_;                                     \
+        prof_t_ = t_;                                                     \
+    } while (0)
+#define KDA_PROF_FLUSH()                                                  \
+    do {                                                                  \
+        if (blockIdx.x == 0 && threadIdx.x == 0)                          \
+            for (int i_ = 0; i_ < 8; ++i_) kda_stage_cycles[i_] = prof_acc_[i_]; \
+    } while (0)
+#else
+#define KDA_PROF_INIT() do {} while (0)
+#define KDA_PROF_MARK(i) do {} while (0)
+#define KDA_PROF_FLUSH() do {} while (0)
+#endif
+
 namespace kda {
 
 namespace {
@@ -49,7 +73,8 @@ struct ChunkCfg {
     static constexpr int LDK = DK + PAD;
     static constexpr int LDV = DVS + PAD;
     static constexpr int LDC = C + PAD;
-    static constexpr int LDL = C + 1;                    // fp32 L / X rows
+    static constexpr int LDL = C + 4;                    // fp32 L / X rows (16-byte aligned)
+    static constexpr int LDY = 20;                       // fp32 16x16 scratch tiles
     static constexpr int NX = (NB - 1) * (NB - 2) / 2;   // block pairs with i - j >= 2
     static constexpr int ES = (int)sizeof(T);
     static constexpr int al(int b) { return (b + 15) / 16 * 16; }
@@ -61,30 +86,41 @@ struct ChunkCfg {
     static constexpr int SZ_KI = SZ_TILE > SZ_L ? SZ_TILE : SZ_L;
     static constexpr int SZ_CC = al(C * LDC * ES);
     static constexpr int SZ_UT = al(DVS * LDC * ES);
-    static constexpr int SZ_Y = al(16 * (C > 16 ? C - 16 : 16) * 4);
+    static constexpr int SZ_Y = al((NB > 1 ? NB - 1 : 1) * 16 * LDY * 4);
     static constexpr int SZ_GT = al(NB * DK * 4);
     static constexpr int SZ_DX = al((NX > 0 ? NX : 1) * DK * 4);
     // offsets
     static constexpr int O_ST = 0;
-    static constexpr int O_KF = O_ST + SZ_ST;       // Kf, then V; U^T reuses both
+    static constexpr int O_KF = O_ST + SZ_ST;       // K F, then V; U^T reuses both
     static constexpr int O_V = O_KF + SZ_TILE;
-    static constexpr int O_QF = O_V + SZ_V;
-    static constexpr int O_KR = O_QF + SZ_TILE;
-    static constexpr int O_KI = O_KR + SZ_TILE;     // K/F, then L and X (fp32)
+    static constexpr int O_QF = O_V + SZ_V;         // Q F
+    static constexpr int O_KH = O_QF + SZ_TILE;     // K e^{G_C - G}
+    static constexpr int O_KI = O_KH + SZ_TILE;     // K / F, then L and X (fp32)
     static constexpr int O_AQK = O_KI + SZ_KI;
-    static constexpr int O_M = O_AQK + SZ_CC;       // M', also the level scratch Y
-    static constexpr int O_W = O_M + SZ_CC;         // -W; before it, block log-totals
-    static constexpr int O_DX = O_W + SZ_GT;        //   and the pair scales (stages 1-2)
+    static constexpr int O_M = O_AQK + SZ_CC;       // M', earlier the inverse's scratch
+    static constexpr int O_W = O_M + SZ_CC;         // -W; earlier block log-totals
+    static constexpr int O_DX = O_W + SZ_GT;        //   and the pair scales
     static constexpr int O_BETA = O_W + SZ_TILE;
     static constexpr int O_P = O_BETA + al(C * 4);
-    static constexpr int O_E = O_P + al(NB * DK * 4);
-    static constexpr int O_GAM = O_E + al(NB * DK * 4);
-    static constexpr int BYTES = O_GAM + al(DK * 4);
+    static constexpr int O_GAM = O_P + al(NB * DK * 4);
+    static constexpr int O_FT = O_GAM + al(DK * 4);
+    static constexpr int BYTES = O_FT + al(NB * DK * 4);
     static_assert(SZ_UT <= SZ_TILE + SZ_V, "U^T must fit in the Kf+V region");
-    static_assert(SZ_Y <= SZ_CC, "level scratch must fit in the M' region");
+    static_assert(SZ_Y <= SZ_CC, "inverse scratch must fit in the M' region");
     static_assert(SZ_GT + SZ_DX <= SZ_TILE, "block totals and pair scales must fit in the W region");
     static constexpr bool fits = BYTES <= kLdsLimit;
 };
+
+// C += A B for 16 x 16 fp32 tiles read from LDS (row-major, leading dims lda,
+// ldb), on one wave with the 16x16x4 fp32 MFMA.
+__device__ __forceinline__ floatx4 mm16_f32(const float* A, int lda, const float* B, int ldb,
+                                            floatx4 c, int lr, int lq) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[lr * lda + 4 * kk + lq],
+                                                 B[(4 * kk + lq) * ldb + lr], c, 0, 0, 0);
+    return c;
+}
 
 // index of block pair (i, j), i - j >= 2, among the scaled-left pairs
 __device__ __forceinline__ constexpr int xidx(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
@@ -99,6 +135,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     using MM = Mma<T>;
     using frag = typename MM::frag;
     constexpr int C = Cfg::C, LDK = Cfg::LDK, LDV = Cfg::LDV, LDC = Cfg::LDC, LDL = Cfg::LDL;
+    constexpr int LDY = Cfg::LDY;
     constexpr int KPL = MM::KPL, KI = MM::KI;
     constexpr int NT = DVS / 16;            // value tiles
     constexpr int CTW = DK / 16 / 4;        // key tiles per wave (state update, W)
@@ -113,19 +150,19 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     T* sV = reinterpret_cast<T*>(smem + Cfg::O_V);
     T* sUT = reinterpret_cast<T*>(smem + Cfg::O_KF);
     T* sQf = reinterpret_cast<T*>(smem + Cfg::O_QF);
-    T* sKr = reinterpret_cast<T*>(smem + Cfg::O_KR);
+    T* sKh = reinterpret_cast<T*>(smem + Cfg::O_KH);
     T* sKi = reinterpret_cast<T*>(smem + Cfg::O_KI);
     float* sL = reinterpret_cast<float*>(smem + Cfg::O_KI);
     T* sAqk = reinterpret_cast<T*>(smem + Cfg::O_AQK);
     T* sM = reinterpret_cast<T*>(smem + Cfg::O_M);
-    float* sY = reinterpret_cast<float*>(smem + Cfg::O_M);
+    float* sYb = reinterpret_cast<float*>(smem + Cfg::O_M);
     T* sW = reinterpret_cast<T*>(smem + Cfg::O_W);
     float* sGt = reinterpret_cast<float*>(smem + Cfg::O_W);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::O_BETA);
     float* sP = reinterpret_cast<float*>(smem + Cfg::O_P);
-    float* sE = reinterpret_cast<float*>(smem + Cfg::O_E);
     float* sGam = reinterpret_cast<float*>(smem + Cfg::O_GAM);
     float* sDx = reinterpret_cast<float*>(smem + Cfg::O_DX);
+    float* sFt = reinterpret_cast<float*>(smem + Cfg::O_FT);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,18 +196,21 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 
     // ---- state: wave w owns key tiles [w*CTW, (w+1)*CTW) x all value tiles --
     floatx4 S[CTW][NT];
-    {
-        const float* s0p = s0 ? s0 + ((int64_t)seq * H + head) * DK * DV : nullptr;
+    if (s0 != nullptr) {
+        const float* s0p = s0 + ((int64_t)seq * H + head) * DK * DV;
 #pragma unroll
         for (int j = 0; j < CTW; ++j)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = (wave * CTW + j) * 16 + 4 * lq + i;
-                    const int n = n0 + nt * 16 + lr;
-                    S[j][nt][i] = s0p ? s0p[(int64_t)c * DV + n] : 0.f;
-                }
+                for (int i = 0; i < 4; ++i)
+                    S[j][nt][i] = s0p[(int64_t)((wave * CTW + j) * 16 + 4 * lq + i) * DV + n0 +
+                                      nt * 16 + lr];
+    } else {
+#pragma unroll
+        for (int j = 0; j < CTW; ++j)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[j][nt] = zero4();
     }
     auto write_state_lds = [&]() {
 #pragma unroll
@@ -187,90 +227,115 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     write_state_lds();
     // A_qk blocks above the diagonal are never written: zero them once
     for (int e = tid; e < C * C; e += kChunkThreads) sAqk[(e / C) * LDC + (e % C)] = from_f<T>(0.f);
-    __syncthreads();
 
     // ---- stage-1 thread layout: CPT channels x 16 tokens of one block ------
     constexpr int CPT = (DK * NB >= 512) ? 2 : 1;
     constexpr int TPB = DK / CPT;
     const bool s1 = tid < NB * TPB;
-    const int blk = tid / TPB;
+    const int blk = s1 ? tid / TPB : 0;
     const int c1 = (tid % TPB) * CPT;
+    using RawC = typename RawVec<T, CPT>::type;
+    using Raw8 = typename RawVec<T, 8>::type;
+    constexpr int VROWS = DVS / 8;                       // 8-column groups per value row
+    constexpr int VPT = (C * VROWS + kChunkThreads - 1) / kChunkThreads;
 
     // U/O tile ownership
     const int rbw = wave / WPR;             // row block of this wave
     const int ntb = wave % WPR;             // first value tile, step WPR
 
+    // ---- one chunk ahead: raw inputs held in registers ---------------------
+    // Addresses are clamped to the last valid token so that every load is
+    // issued unconditionally; rows past the sequence end are zeroed on use.
+    RawC pg[16], pk[16], pq[16];
+    Raw8 pv[VPT];
+    T pb;
+    auto issue_loads = [&](int64_t tok0n, int validn) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int r = blk * 16 + t;
+            const int64_t tok = tok0n + (r < validn ? r : validn - 1);
+            pg[t] = *reinterpret_cast<const RawC*>(g + (tok * H + head) * DK + c1);
+            pk[t] = *reinterpret_cast<const RawC*>(k + tok * stride + (int64_t)head * DK + c1);
+            pq[t] = *reinterpret_cast<const RawC*>(q + tok * stride + (int64_t)head * DK + c1);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            int e = tid + u * kChunkThreads;
+            e = e < C * VROWS ? e : C * VROWS - 1;
+            const int r = e / VROWS;
+            const int64_t tok = tok0n + (r < validn ? r : validn - 1);
+            pv[u] = *reinterpret_cast<const Raw8*>(v + tok * stride + (int64_t)head * DV + n0 +
+                                                  (e % VROWS) * 8);
+        }
+        pb = beta[(tok0n + (tid < validn ? tid : validn - 1)) * H + head];
+    };
+    if (n_chunks > 0) {
+        const int64_t len = t_end - t_begin;
+        issue_loads(t_begin, (int)(len < C ? len : C));
+    }
+    __syncthreads();
+    KDA_PROF_INIT();
+
     for (int64_t ci = 0; ci < n_chunks; ++ci) {
         const int64_t tok0 = t_begin + ci * C;
         const int valid = (int)((t_end - tok0) < C ? (t_end - tok0) : C);
 
-        // ================= stage 1a: loads, block log-decay totals ===========
-        float gr[16][CPT], kr[16][CPT], qr[16][CPT];
+        // ================= stage 1: decay factors and operand tiles ==========
+        // pass A: per (block, channel) log-decay totals (log2 units)
         if (s1) {
             float gs[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) gs[j] = 0.f;
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                const int r = blk * 16 + t;
-                if (r < valid) {
-                    const int64_t tok = tok0 + r;
-                    const T* gp = g + (tok * H + head) * DK + c1;
-                    const T* kp = k + tok * stride + (int64_t)head * DK + c1;
-                    const T* qp = q + tok * stride + (int64_t)head * DK + c1;
-                    if constexpr (CPT == 2) {
-                        load2(gp, gr[t][0], gr[t][1]);
-                        load2(kp, kr[t][0], kr[t][1]);
-                        load2(qp, qr[t][0], qr[t][1]);
-                    } else {
-                        gr[t][0] = to_f(gp[0]);
-                        kr[t][0] = to_f(kp[0]);
-                        qr[t][0] = to_f(qp[0]);
-                    }
+                const bool ok = blk * 16 + t < valid;
+                float gv[CPT];
+                RawVec<T, CPT>::unpack(pg[t], gv);
 #pragma unroll
-                    for (int j = 0; j < CPT; ++j) gr[t][j] = clamp_log_decay(gr[t][j]) * kLog2e;
-                } else {
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j) { gr[t][j] = 0.f; kr[t][j] = 0.f; qr[t][j] = 0.f; }
-                }
-#pragma unroll
-                for (int j = 0; j < CPT; ++j) gs[j] += gr[t][j];
+                for (int j = 0; j < CPT; ++j) gs[j] += ok ? clamp_log_decay(gv[j]) * kLog2e : 0.f;
             }
 #pragma unroll
             for (int j = 0; j < CPT; ++j) sGt[blk * DK + c1 + j] = gs[j];
         }
-        // value slice, token-major, 8 columns per thread-step
-        for (int e = tid; e < C * (DVS / 8); e += kChunkThreads) {
-            const int r = e / (DVS / 8);
-            const int c8 = (e % (DVS / 8)) * 8;
-            float vv[8];
-            if (r < valid) {
-                load8(v + (tok0 + r) * stride + (int64_t)head * DV + n0 + c8, vv);
-            } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) vv[i] = 0.f;
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * kChunkThreads;
+            if (e < C * VROWS) {
+                const int r = e / VROWS;
+                float vv[8];
+                RawVec<T, 8>::unpack(pv[u], vv);
+                if (r >= valid) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) vv[i] = 0.f;
+                }
+                store8(sV + r * LDV + (e % VROWS) * 8, vv);
             }
-            store8(sV + r * LDV + c8, vv);
         }
-        if (tid < C) sBeta[tid] = tid < valid ? to_f(beta[(tok0 + tid) * H + head]) : 0.f;
+        if (tid < C) sBeta[tid] = tid < valid ? to_f(pb) : 0.f;
         __syncthreads();
+        KDA_PROF_MARK(0);
 
-        // ================= stage 1b: decay factors and operand tiles ========
+        // pass B: block tables, then one sweep over the block's 16 tokens with
+        // G the local cumulative log-decay, F = 2^G, 1/F = 2^-G
         if (s1) {
+            float Fb[CPT], Eb[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
                 const int c = c1 + j;
                 float Ft[NB];
 #pragma unroll
                 for (int m = 0; m < NB; ++m) Ft[m] = fast_exp2(sGt[m * DK + c]);
-                float P = 1.f, E = 1.f;
+                float P = 1.f, E = 1.f, F0 = 1.f;
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
                     if (m < blk) P *= Ft[m];
                     if (m > blk) E *= Ft[m];
+                    if (m == blk) F0 = Ft[m];
                 }
+                Fb[j] = F0;
+                Eb[j] = E;
                 sP[blk * DK + c] = P;
-                sE[blk * DK + c] = E;
+                sFt[blk * DK + c] = F0;
                 if (blk == 0) {
                     float gam = 1.f;
 #pragma unroll
@@ -286,131 +351,172 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                             sDx[xidx(i2, j2) * DK + c] = dx;
                         }
                 }
-                float Ftb = Ft[0];
+            }
+            float G[CPT];
 #pragma unroll
-                for (int m = 1; m < NB; ++m) if (m == blk) Ftb = Ft[m];
-                float G = 0.f;
+            for (int j = 0; j < CPT; ++j) G[j] = 0.f;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    G += gr[t][j];
-                    const float F = fast_exp2(G);
-                    const float Fi = fast_exp2(-G);
-                    const float Rs = Fi * Ftb;
-                    const int r = blk * 16 + t;
-                    sKf[r * LDK + c] = from_f<T>(kr[t][j] * F);
-                    sQf[r * LDK + c] = from_f<T>(qr[t][j] * F);
-                    sKi[r * LDK + c] = from_f<T>(kr[t][j] * Fi);
-                    sKr[r * LDK + c] = from_f<T>(kr[t][j] * Rs);
+            for (int t = 0; t < 16; ++t) {
+                const int r = blk * 16 + t;
+                const bool ok = r < valid;
+                float gv[CPT], kv[CPT], qv[CPT], kf[CPT], qf[CPT], ki[CPT], kh[CPT];
+                RawVec<T, CPT>::unpack(pg[t], gv);
+                RawVec<T, CPT>::unpack(pk[t], kv);
+                RawVec<T, CPT>::unpack(pq[t], qv);
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) {
+                    G[j] += ok ? clamp_log_decay(gv[j]) * kLog2e : 0.f;
+                    const float F = fast_exp2(G[j]);
+                    const float Fi = fast_exp2(-G[j]);
+                    const float kk = ok ? kv[j] : 0.f;
+                    const float qq = ok ? qv[j] : 0.f;
+                    kf[j] = kk * F;
+                    qf[j] = qq * F;
+                    ki[j] = kk * Fi;
+                    kh[j] = (ki[j] * Fb[j]) * Eb[j];   // k e^{G_C - G_r}: both factors <= 1 in turn
                 }
+                RawVec<T, CPT>::store(sKf + r * LDK + c1, kf);
+                RawVec<T, CPT>::store(sQf + r * LDK + c1, qf);
+                RawVec<T, CPT>::store(sKi + r * LDK + c1, ki);
+                RawVec<T, CPT>::store(sKh + r * LDK + c1, kh);
             }
         }
         __syncthreads();
+        // the next chunk's inputs stream in while this chunk computes
+        if (ci + 1 < n_chunks) {
+            const int64_t rem = t_end - (tok0 + C);
+            issue_loads(tok0 + C, (int)(rem < C ? rem : C));
+        }
+        KDA_PROF_MARK(1);
 
         // ================= stage 2: A_kk, A_qk tiles (MFMA) ==================
-        constexpr int NPAIR = NB * (NB + 1) / 2;
-        constexpr int NT2 = 2 * NPAIR;
-        constexpr int T2W = (NT2 + 3) / 4;
-        floatx4 accA[T2W];
+        // Wave w computes one kind (A_kk for even w, A_qk for odd w) for row
+        // blocks {w/2, NB-1-w/2} (NB = 4) or {w/2} (NB = 2): five tiles each.
+        // Right operand: same block -> k/F; earlier block j -> (k/F) * F_j.
+        // Left operand scaled by the block totals strictly between j and i.
+        constexpr int RPW = NB >= 4 ? 2 : 1;
+        constexpr int KS = DK / KI;
+        const int kind = wave & 1;
+        const bool s2 = NB > 1 || wave < 2;
+        floatx4 accA[RPW][NB];
 #pragma unroll
-        for (int u = 0; u < T2W; ++u) {
-            accA[u] = zero4();
-            const int tau = wave + 4 * u;
-            if (tau < NT2) {
-                const int kind = tau & 1;            // 0: A_kk, 1: A_qk
-                const int p = tau >> 1;
-                int i = 0;
-                while ((i + 1) * (i + 2) / 2 <= p) ++i;
-                const int j = p - i * (i + 1) / 2;
-                const T* left = (kind ? sQf : sKf) + (i * 16 + lr) * LDK;
-                const T* right = (j == i ? sKi : sKr) + (j * 16 + lr) * LDK;
-                const bool scaled = (i - j) >= 2;
-                const float* dx = scaled ? sDx + xidx(i, j) * DK : nullptr;
+        for (int sl = 0; sl < RPW; ++sl) {
+            const int i = sl == 0 ? (wave >> 1) : NB - 1 - (wave >> 1);
+            const T* left = (kind ? sQf : sKf) + (i * 16 + lr) * LDK + KPL * lq;
+            frag la[KS];
 #pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += KI) {
-                    const int kk = k0 + KPL * lq;
-                    frag a = MM::load(left + kk);
-                    if (scaled) {
+            for (int ks = 0; ks < KS; ++ks) la[ks] = MM::load(left + ks * KI);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                accA[sl][j] = zero4();
+                if (!s2 || j > i) continue;
+                const T* right = sKi + (j * 16 + lr) * LDK + KPL * lq;
+                const float* fr = sFt + j * DK + KPL * lq;
+                const float* dx = sDx + (i - j >= 2 ? xidx(i, j) : 0) * DK + KPL * lq;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    frag a = la[ks];
+                    if (i - j >= 2) {
                         float av[KPL];
                         MM::unpack(a, av);
 #pragma unroll
-                        for (int e = 0; e < KPL; ++e) av[e] *= dx[kk + e];
+                        for (int e = 0; e < KPL; ++e) av[e] *= dx[ks * KI + e];
                         a = MM::pack(av);
                     }
-                    const frag b = MM::load(right + kk);
-                    accA[u] = MM::mma(a, b, accA[u]);
+                    frag b = MM::load(right + ks * KI);
+                    if (j < i) {
+                        float bv[KPL];
+                        MM::unpack(b, bv);
+#pragma unroll
+                        for (int e = 0; e < KPL; ++e) bv[e] *= fr[ks * KI + e];
+                        b = MM::pack(bv);
+                    }
+                    accA[sl][j] = MM::mma(a, b, accA[sl][j]);
                 }
             }
         }
         __syncthreads();   // every read of K/F done before L overwrites it
+        if (s2) {
 #pragma unroll
-        for (int u = 0; u < T2W; ++u) {
-            const int tau = wave + 4 * u;
-            if (tau < NT2) {
-                const int kind = tau & 1;
-                const int p = tau >> 1;
-                int i = 0;
-                while ((i + 1) * (i + 2) / 2 <= p) ++i;
-                const int j = p - i * (i + 1) / 2;
+            for (int sl = 0; sl < RPW; ++sl) {
+                const int i = sl == 0 ? (wave >> 1) : NB - 1 - (wave >> 1);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int rl = 4 * lq + ii, sl = lr;
-                    const int r = i * 16 + rl, s = j * 16 + sl;
-                    if (kind == 0) {
-                        const bool keep = (j < i) || (sl < rl);
-                        sL[r * LDL + s] = keep ? sBeta[r] * accA[u][ii] : 0.f;
-                    } else {
-                        const bool keep = (j < i) || (sl <= rl);
-                        sAqk[r * LDC + s] = from_f<T>(keep ? accA[u][ii] : 0.f);
+                for (int j = 0; j < NB; ++j) {
+                    if (j > i) continue;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int rl = 4 * lq + ii, sl2 = lr;
+                        const int r = i * 16 + rl, s = j * 16 + sl2;
+                        if (kind == 0) {
+                            const bool keep = (j < i) || (sl2 < rl);
+                            sL[r * LDL + s] = keep ? sBeta[r] * accA[sl][j][ii] : 0.f;
+                        } else {
+                            const bool keep = (j < i) || (sl2 <= rl);
+                            sAqk[r * LDC + s] = from_f<T>(keep ? accA[sl][j][ii] : 0.f);
+                        }
                     }
                 }
             }
         }
         __syncthreads();
+        KDA_PROF_MARK(2);
 
         // ================= stage 3: X = (I + L)^{-1}, M' = X diag(beta) =====
-        if (wave < NB && lane < 16) {   // diagonal blocks: forward substitution
+        // Diagonal 16x16 blocks by forward substitution (wave b, lane = column),
+        // updating the remaining rows after each solved row.
+        if (wave < NB && lane < 16) {
             const int b0 = wave * 16;
             const int cc = lane;
-            float xcol[16];
+            float acc[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == cc) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) acc[r] = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= sL[(b0 + r) * LDL + b0 + m] * xcol[m];
-                xcol[r] = acc;
+            for (int m = 0; m < 16; ++m) {
+                const float xm = acc[m];
+#pragma unroll
+                for (int r = m + 1; r < 16; ++r) acc[r] -= sL[(b0 + r) * LDL + b0 + m] * xm;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sL[(b0 + r) * LDL + b0 + cc] = xcol[r];
+            for (int r = 0; r < 16; ++r) sL[(b0 + r) * LDL + b0 + cc] = acc[r];
         }
         __syncthreads();
+        // Off-diagonal blocks by block rows: X_ij = -X_ii sum_{m=j}^{i-1} L_im X_mj,
+        // wave j computing the (i, j) tile with fp32 MFMA.
 #pragma unroll
-        for (int i = 1; i < NB; ++i) {          // block rows, one level each
-            const int w16 = 16 * i;
-            for (int e = tid; e < 16 * w16; e += kChunkThreads) {
-                const int r = e / w16, col = e % w16;
-                float acc = 0.f;
-                for (int s = (col / 16) * 16; s < w16; ++s)
-                    acc += sL[(w16 + r) * LDL + s] * sL[s * LDL + col];
-                sY[r * w16 + col] = acc;
+        for (int i = 1; i < NB; ++i) {
+            float* yw = sYb + wave * 16 * LDY;
+            if (wave < i) {
+                floatx4 y = zero4();
+                for (int m = wave; m < i; ++m)
+                    y = mm16_f32(sL + (16 * i) * LDL + 16 * m, LDL, sL + (16 * m) * LDL + 16 * wave,
+                                 LDL, y, lr, lq);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) yw[(4 * lq + ii) * LDY + lr] = y[ii];
             }
             __syncthreads();
-            for (int e = tid; e < 16 * w16; e += kChunkThreads) {
-                const int r = e / w16, col = e % w16;
-                float acc = 0.f;
+            if (wave < i) {
+                const floatx4 x = mm16_f32(sL + (16 * i) * LDL + 16 * i, LDL, yw, LDY, zero4(), lr, lq);
 #pragma unroll
-                for (int m = 0; m < 16; ++m) acc += sL[(w16 + r) * LDL + w16 + m] * sY[m * w16 + col];
-                sL[(w16 + r) * LDL + col] = -acc;
+                for (int ii = 0; ii < 4; ++ii) sL[(16 * i + 4 * lq + ii) * LDL + 16 * wave + lr] = -x[ii];
             }
             __syncthreads();
         }
-        for (int e = tid; e < C * C; e += kChunkThreads) {
-            const int r = e / C, s = e % C;
-            float val = 0.f;
-            if (s < r) val = sL[r * LDL + s] * sBeta[s];
-            else if (s == r) val = sBeta[s];
-            sM[r * LDC + s] = from_f<T>(val);
+        {
+            constexpr int PER = C * C / kChunkThreads > 0 ? C * C / kChunkThreads : 1;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                const int e = tid + u * kChunkThreads;
+                if (e < C * C) {
+                    const int r = e / C, s = e % C;
+                    const float bs = sBeta[s];
+                    float val = s < r ? sL[r * LDL + s] * bs : 0.f;
+                    val = s == r ? bs : val;
+                    sM[r * LDC + s] = from_f<T>(val);
+                }
+            }
         }
         __syncthreads();
+        KDA_PROF_MARK(3);
 
         // ================= stage 4: -W = -M'(K e^G) and Utilde = M'V ========
         // W tiles: wave owns key tiles (CTW of them) for all row blocks
@@ -465,6 +571,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             }
         }
         __syncthreads();   // -W complete; Kf, V, M' no longer read
+        KDA_PROF_MARK(4);
 
         // ================= stage 5: U += (-W) S0,  O = (Q e^G) S0 ===========
 #pragma unroll
@@ -494,6 +601,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             for (int ii = 0; ii < 4; ++ii) p[ii] = from_f<T>(accU[j][ii]);
         }
         __syncthreads();
+        KDA_PROF_MARK(5);
 
         // ================= stage 6: O += A_qk U;  S = diag(e^{G_C}) S + K^T U
 #pragma unroll
@@ -530,13 +638,12 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             }
 #pragma unroll
             for (int ks = 0; ks < C / KI; ++ks) {
-                // A[m = c][k = s] = Kr[s][c] * E[block(s)][c]  (transposed read)
+                // A[m = c][k = s] = Khat[s][c]  (transposed read)
                 const int sb = ks * KI + KPL * lq;
                 const int c = ct * 16 + lr;
-                const float ef = sE[(sb / 16) * DK + c];
                 float av[KPL];
 #pragma unroll
-                for (int e = 0; e < KPL; ++e) av[e] = to_f(sKr[(sb + e) * LDK + c]) * ef;
+                for (int e = 0; e < KPL; ++e) av[e] = to_f(sKh[(sb + e) * LDK + c]);
                 const frag a = MM::pack(av);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
@@ -545,7 +652,9 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
         }
         write_state_lds();
         __syncthreads();
+        KDA_PROF_MARK(6);
     }
+    KDA_PROF_FLUSH();
 
     // ---- final state ---------------------------------------------------------
     if (sT) {

@@ -68,6 +68,44 @@ __device__ __forceinline__ void store2(__bf16* p, float a, float b) {
     *reinterpret_cast<bf16x2*>(p) = t;
 }
 
+// ---- raw vectors of N I/O elements, kept unconverted in registers -------------
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+
+template <typename T, int N>
+struct RawVec;
+
+template <int N, typename V, typename E>
+struct RawVecImpl {
+    typedef V type;
+    static __device__ __forceinline__ void unpack(const V& r, float v[N]) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = (float)r[i];
+    }
+    static __device__ __forceinline__ void store(E* p, const float v[N]) {
+        V r;
+#pragma unroll
+        for (int i = 0; i < N; ++i) r[i] = (E)v[i];
+        *reinterpret_cast<V*>(p) = r;
+    }
+};
+template <>
+struct RawVec<__bf16, 1> {
+    typedef __bf16 type;
+    static __device__ __forceinline__ void unpack(const __bf16& r, float v[1]) { v[0] = (float)r; }
+    static __device__ __forceinline__ void store(__bf16* p, const float v[1]) { *p = (__bf16)v[0]; }
+};
+template <>
+struct RawVec<float, 1> {
+    typedef float type;
+    static __device__ __forceinline__ void unpack(const float& r, float v[1]) { v[0] = r; }
+    static __device__ __forceinline__ void store(float* p, const float v[1]) { *p = v[0]; }
+};
+template <> struct RawVec<__bf16, 2> : RawVecImpl<2, bf16x2, __bf16> {};
+template <> struct RawVec<__bf16, 8> : RawVecImpl<8, bf16x8, __bf16> {};
+template <> struct RawVec<float, 2> : RawVecImpl<2, floatx2, float> {};
+template <> struct RawVec<float, 8> : RawVecImpl<8, floatx8, float> {};
+
 // ---- math --------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
