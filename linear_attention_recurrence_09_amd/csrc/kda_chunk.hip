@@ -38,10 +38,10 @@
 // Optional stage timing (profiling builds define KDA_STAGE_PROFILE and the
 // array; workgroup 0, thread 0 records the cycles spent in each stage).
 #ifdef KDA_STAGE_PROFILE
-extern __device__ unsigned long long kda_stage_cycles[8];
+extern __device__ unsigned long long kda_stage_cycles[16];
 #define KDA_PROF_INIT()                                          \
     unsigned long long prof_t_ = __builtin_readcyclecounter();  \
-    unsigned long long prof_acc_[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+    unsigned long long prof_acc_[16] = {}
 #define KDA_PROF_MARK(i)                                                  \
     do {                                                                  \
         const unsigned long long t_ = __builtin_readcyclecounter();      \
@@ -51,7 +51,7 @@ extern __device__ unsigned long long kda_stage_cycles[8];
 #define KDA_PROF_FLUSH()                                                  \
     do {                                                                  \
         if (blockIdx.x == 0 && threadIdx.x == 0)                          \
-            for (int i_ = 0; i_ < 8; ++i_) kda_stage_cycles[i_] = prof_acc_[i_]; \
+            for (int i_ = 0; i_ < 16; ++i_) kda_stage_cycles[i_] = prof_acc_[i_]; \
     } while (0)
 #else
 #define KDA_PROF_INIT() do {} while (0)
@@ -87,43 +87,129 @@ struct ChunkCfg {
     static constexpr int SZ_CC = al(C * LDC * ES);
     static constexpr int SZ_UT = al(DVS * LDC * ES);
     static constexpr int SZ_Y = al((NB > 1 ? NB - 1 : 1) * 16 * LDY * 4);
-    static constexpr int SZ_GT = al(NB * DK * 4);
     static constexpr int SZ_DX = al((NX > 0 ? NX : 1) * DK * 4);
     // offsets
-    static constexpr int O_ST = 0;
+    static constexpr int O_ST = 0;                  // S^T (operand copy of the state)
     static constexpr int O_KF = O_ST + SZ_ST;       // K F, then V; U^T reuses both
     static constexpr int O_V = O_KF + SZ_TILE;
     static constexpr int O_QF = O_V + SZ_V;         // Q F
-    static constexpr int O_KH = O_QF + SZ_TILE;     // K e^{G_C - G}
-    static constexpr int O_KI = O_KH + SZ_TILE;     // K / F, then L and X (fp32)
+    static constexpr int O_KR = O_QF + SZ_TILE;     // K e^{G_end(block) - G}
+    static constexpr int O_KI = O_KR + SZ_TILE;     // K / F, then L and X (fp32)
     static constexpr int O_AQK = O_KI + SZ_KI;
-    static constexpr int O_M = O_AQK + SZ_CC;       // M', earlier the inverse's scratch
-    static constexpr int O_W = O_M + SZ_CC;         // -W; earlier block log-totals
-    static constexpr int O_DX = O_W + SZ_GT;        //   and the pair scales
+    static constexpr int O_W = O_AQK + SZ_CC;       // pair scales (stages 1-2), inverse
+                                                    // scratch (stage 3), then -W
     static constexpr int O_BETA = O_W + SZ_TILE;
     static constexpr int O_P = O_BETA + al(C * 4);
-    static constexpr int O_GAM = O_P + al(NB * DK * 4);
-    static constexpr int O_FT = O_GAM + al(DK * 4);
-    static constexpr int BYTES = O_FT + al(NB * DK * 4);
+    static constexpr int O_E = O_P + al(NB * DK * 4);
+    static constexpr int O_GAM = O_E + al(NB * DK * 4);
+    static constexpr int BYTES = O_GAM + al(DK * 4);
     static_assert(SZ_UT <= SZ_TILE + SZ_V, "U^T must fit in the Kf+V region");
-    static_assert(SZ_Y <= SZ_CC, "inverse scratch must fit in the M' region");
-    static_assert(SZ_GT + SZ_DX <= SZ_TILE, "block totals and pair scales must fit in the W region");
+    static_assert(SZ_Y <= SZ_TILE && SZ_DX <= SZ_TILE, "scratch must fit in the W region");
     static constexpr bool fits = BYTES <= kLdsLimit;
 };
+
+// index of block pair (i, j), i - j >= 2, among the scaled-left pairs
+__device__ __forceinline__ constexpr int xidx(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
 
 // C += A B for 16 x 16 fp32 tiles read from LDS (row-major, leading dims lda,
 // ldb), on one wave with the 16x16x4 fp32 MFMA.
 __device__ __forceinline__ floatx4 mm16_f32(const float* A, int lda, const float* B, int ldb,
                                             floatx4 c, int lr, int lq) {
+    float a[4], b[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[lr * lda + 4 * kk + lq],
-                                                 B[(4 * kk + lq) * ldb + lr], c, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+        a[kk] = A[lr * lda + 4 * kk + lq];
+        b[kk] = B[(4 * kk + lq) * ldb + lr];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b[kk], c, 0, 0, 0);
     return c;
 }
 
-// index of block pair (i, j), i - j >= 2, among the scaled-left pairs
-__device__ __forceinline__ constexpr int xidx(int i, int j) { return (i - 2) * (i - 1) / 2 + j; }
+// Stage-2 schedule: wave W computes one kind of intra-chunk matrix (A_kk for
+// even W, A_qk for odd W) over row blocks {W/2, NB-1-W/2} (NB = 4) or {W/2}
+// (NB = 2): five tiles each for NB = 4.  Templated on W so that every tile
+// index, loop bound and scaling choice is a compile-time constant.
+template <int NB, int W>
+struct S2Plan {
+    static constexpr int kind = W & 1;
+    static constexpr int rows = NB >= 4 ? 2 : ((NB == 2 || W < 2) ? 1 : 0);
+    static constexpr int row(int sl) { return NB >= 4 ? (sl == 0 ? (W >> 1) : NB - 1 - (W >> 1)) : (W >> 1); }
+    static constexpr int slot(int sl, int j) { return sl == 0 ? j : row(0) + 1 + j; }
+};
+constexpr int kMaxS2Tiles = 5;
+
+template <typename T, int DK, int NB, int W, int LDK>
+__device__ __forceinline__ void stage2_compute(const T* sKf, const T* sQf, const T* sKi,
+                                               const T* sKr, const float* sDx,
+                                               floatx4 (&acc)[kMaxS2Tiles], int lr, int lq) {
+    using MM = Mma<T>;
+    using frag = typename MM::frag;
+    using P = S2Plan<NB, W>;
+    constexpr int KPL = MM::KPL, KI = MM::KI, KS = DK / KI;
+#pragma unroll
+    for (int sl = 0; sl < P::rows; ++sl) {
+        const int i = P::row(sl);
+        const T* left = (P::kind ? sQf : sKf) + (i * 16 + lr) * LDK + KPL * lq;
+        frag la[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) la[ks] = MM::load(left + ks * KI);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if (j > i) continue;
+            floatx4 a4 = zero4();
+            // right: same block -> k / F; earlier block -> k e^{G_end(j) - G}
+            const T* right = (j == i ? sKi : sKr) + (j * 16 + lr) * LDK + KPL * lq;
+            const float* dx = sDx + (i - j >= 2 ? xidx(i, j) : 0) * DK + KPL * lq;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                frag a = la[ks];
+                if (i - j >= 2) {          // left: block totals strictly between j and i
+                    float av[KPL];
+                    MM::unpack(a, av);
+#pragma unroll
+                    for (int e = 0; e < KPL; ++e) av[e] *= dx[ks * KI + e];
+                    a = MM::pack(av);
+                }
+                a4 = MM::mma(a, MM::load(right + ks * KI), a4);
+            }
+            acc[P::slot(sl, j)] = a4;
+        }
+    }
+}
+
+template <typename T, int NB, int W, int LDC, int LDL>
+__device__ __forceinline__ void stage2_write(const floatx4 (&acc)[kMaxS2Tiles], float* sL, T* sAqk,
+                                             const float* sBeta, int lr, int lq) {
+    using P = S2Plan<NB, W>;
+#pragma unroll
+    for (int sl = 0; sl < P::rows; ++sl) {
+        const int i = P::row(sl);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if (j > i) continue;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int rl = 4 * lq + ii;
+                const int r = i * 16 + rl, s = j * 16 + lr;
+                const float a = acc[P::slot(sl, j)][ii];
+                if (P::kind == 0) {
+                    // off-diagonal L tiles in place; a diagonal tile's strictly lower
+                    // part goes transposed into its upper triangle, so that the
+                    // forward substitution reads columns of L as contiguous rows
+                    if (j < i) {
+                        sL[r * LDL + s] = sBeta[r] * a;
+                    } else if (lr < rl) {
+                        sL[(i * 16 + lr) * LDL + i * 16 + rl] = sBeta[r] * a;
+                    }
+                } else {
+                    const bool keep = (j < i) || (lr <= rl);
+                    sAqk[r * LDC + s] = from_f<T>(keep ? a : 0.f);
+                }
+            }
+        }
+    }
+}
 
 template <typename T, int DK, int DVS, int NB>
 __global__ void __launch_bounds__(kChunkThreads)
@@ -135,12 +221,13 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     using MM = Mma<T>;
     using frag = typename MM::frag;
     constexpr int C = Cfg::C, LDK = Cfg::LDK, LDV = Cfg::LDV, LDC = Cfg::LDC, LDL = Cfg::LDL;
-    constexpr int LDY = Cfg::LDY;
+    constexpr int LDY = Cfg::LDY, ES = Cfg::ES;
     constexpr int KPL = MM::KPL, KI = MM::KI;
     constexpr int NT = DVS / 16;            // value tiles
     constexpr int CTW = DK / 16 / 4;        // key tiles per wave (state update, W)
     constexpr int WPR = 4 / NB;             // waves per row block (U, O)
     constexpr int NTW = (NT + WPR - 1) / WPR;   // value tiles per wave (U, O)
+    constexpr int NKS = C / KI;             // MFMA steps over a chunk's tokens
     static_assert(DK % 64 == 0, "tile split");
     static_assert(C % KI == 0, "chunk must be a multiple of the MFMA depth");
 
@@ -150,19 +237,17 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     T* sV = reinterpret_cast<T*>(smem + Cfg::O_V);
     T* sUT = reinterpret_cast<T*>(smem + Cfg::O_KF);
     T* sQf = reinterpret_cast<T*>(smem + Cfg::O_QF);
-    T* sKh = reinterpret_cast<T*>(smem + Cfg::O_KH);
+    T* sKr = reinterpret_cast<T*>(smem + Cfg::O_KR);
     T* sKi = reinterpret_cast<T*>(smem + Cfg::O_KI);
     float* sL = reinterpret_cast<float*>(smem + Cfg::O_KI);
     T* sAqk = reinterpret_cast<T*>(smem + Cfg::O_AQK);
-    T* sM = reinterpret_cast<T*>(smem + Cfg::O_M);
-    float* sYb = reinterpret_cast<float*>(smem + Cfg::O_M);
     T* sW = reinterpret_cast<T*>(smem + Cfg::O_W);
-    float* sGt = reinterpret_cast<float*>(smem + Cfg::O_W);
+    float* sDx = reinterpret_cast<float*>(smem + Cfg::O_W);
+    float* sYb = reinterpret_cast<float*>(smem + Cfg::O_W);
     float* sBeta = reinterpret_cast<float*>(smem + Cfg::O_BETA);
     float* sP = reinterpret_cast<float*>(smem + Cfg::O_P);
+    float* sE = reinterpret_cast<float*>(smem + Cfg::O_E);
     float* sGam = reinterpret_cast<float*>(smem + Cfg::O_GAM);
-    float* sDx = reinterpret_cast<float*>(smem + Cfg::O_DX);
-    float* sFt = reinterpret_cast<float*>(smem + Cfg::O_FT);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -228,15 +313,18 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     // A_qk blocks above the diagonal are never written: zero them once
     for (int e = tid; e < C * C; e += kChunkThreads) sAqk[(e / C) * LDC + (e % C)] = from_f<T>(0.f);
 
-    // ---- stage-1 thread layout: CPT channels x 16 tokens of one block ------
-    constexpr int CPT = (DK * NB >= 512) ? 2 : 1;
-    constexpr int TPB = DK / CPT;
-    const bool s1 = tid < NB * TPB;
-    const int blk = s1 ? tid / TPB : 0;
-    const int c1 = (tid % TPB) * CPT;
+    // ---- stage-1 lane layout: wave w owns channels [w*DK/4, (w+1)*DK/4) for all
+    // blocks; lane = (block, channel group of CPT channels) -----------------
+    constexpr int LPB = 64 / NB;                          // lanes per block
+    constexpr int CW = DK / 4;                            // channels per wave
+    constexpr int CPT = CW / LPB > 0 ? CW / LPB : 1;      // channels per lane
+    const int blk = lane / LPB;
+    const int li = lane % LPB;
+    const bool s1 = li * CPT < CW;
+    const int c1 = wave * CW + (s1 ? li * CPT : 0);
     using RawC = typename RawVec<T, CPT>::type;
     using Raw8 = typename RawVec<T, 8>::type;
-    constexpr int VROWS = DVS / 8;                       // 8-column groups per value row
+    constexpr int VROWS = DVS / 8;                        // 8-column groups per value row
     constexpr int VPT = (C * VROWS + kChunkThreads - 1) / kChunkThreads;
 
     // U/O tile ownership
@@ -244,30 +332,35 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     const int ntb = wave % WPR;             // first value tile, step WPR
 
     // ---- one chunk ahead: raw inputs held in registers ---------------------
-    // Addresses are clamped to the last valid token so that every load is
-    // issued unconditionally; rows past the sequence end are zeroed on use.
+    // Buffer resources span the chunk's valid rows, so rows past the end of
+    // the sequence read as zero: k = q = v = 0, g = 0 (no decay), beta = 0,
+    // i.e. identity steps.
     RawC pg[16], pk[16], pq[16];
     Raw8 pv[VPT];
     T pb;
+    const int g_row = H * DK * ES, kv_row = (int)(stride * ES);
+    const int g_lane = (blk * 16 * H * DK + c1) * ES;
+    const int k_lane = (int)((blk * 16 * stride + c1) * ES);
     auto issue_loads = [&](int64_t tok0n, int validn) {
+        const rsrc_t rg = make_rsrc(g + (tok0n * H + head) * DK, (uint32_t)(validn * g_row));
+        const rsrc_t rk = make_rsrc(k + tok0n * stride + (int64_t)head * DK, (uint32_t)(validn * kv_row));
+        const rsrc_t rq = make_rsrc(q + tok0n * stride + (int64_t)head * DK, (uint32_t)(validn * kv_row));
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const int r = blk * 16 + t;
-            const int64_t tok = tok0n + (r < validn ? r : validn - 1);
-            pg[t] = *reinterpret_cast<const RawC*>(g + (tok * H + head) * DK + c1);
-            pk[t] = *reinterpret_cast<const RawC*>(k + tok * stride + (int64_t)head * DK + c1);
-            pq[t] = *reinterpret_cast<const RawC*>(q + tok * stride + (int64_t)head * DK + c1);
+            pg[t] = BufLoad<T, CPT>::load(rg, g_lane + t * g_row);
+            pk[t] = BufLoad<T, CPT>::load(rk, k_lane + t * kv_row);
+            pq[t] = BufLoad<T, CPT>::load(rq, k_lane + t * kv_row);
         }
+        const rsrc_t rv = make_rsrc(v + tok0n * stride + (int64_t)head * DV + n0,
+                                    (uint32_t)(validn * kv_row));
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             int e = tid + u * kChunkThreads;
             e = e < C * VROWS ? e : C * VROWS - 1;
-            const int r = e / VROWS;
-            const int64_t tok = tok0n + (r < validn ? r : validn - 1);
-            pv[u] = *reinterpret_cast<const Raw8*>(v + tok * stride + (int64_t)head * DV + n0 +
-                                                  (e % VROWS) * 8);
+            pv[u] = BufLoad<T, 8>::load(rv, (e / VROWS) * kv_row + (e % VROWS) * 8 * ES);
         }
-        pb = beta[(tok0n + (tid < validn ? tid : validn - 1)) * H + head];
+        const rsrc_t rb = make_rsrc(beta + tok0n * H + head, (uint32_t)(validn * H * ES));
+        pb = BufLoad<T, 1>::load(rb, (tid < C ? tid : 0) * H * ES);
     };
     if (n_chunks > 0) {
         const int64_t len = t_end - t_begin;
@@ -278,53 +371,27 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 
     for (int64_t ci = 0; ci < n_chunks; ++ci) {
         const int64_t tok0 = t_begin + ci * C;
-        const int valid = (int)((t_end - tok0) < C ? (t_end - tok0) : C);
 
         // ================= stage 1: decay factors and operand tiles ==========
-        // pass A: per (block, channel) log-decay totals (log2 units)
-        if (s1) {
-            float gs[CPT];
+        // Block log-decay totals (log2 units) per lane, exchanged across the
+        // lanes holding the same channels in the other blocks.
+        {
+            float gt[CPT];
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) gs[j] = 0.f;
+            for (int j = 0; j < CPT; ++j) gt[j] = 0.f;
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                const bool ok = blk * 16 + t < valid;
                 float gv[CPT];
                 RawVec<T, CPT>::unpack(pg[t], gv);
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) gs[j] += ok ? clamp_log_decay(gv[j]) * kLog2e : 0.f;
+                for (int j = 0; j < CPT; ++j) gt[j] += clamp_log_decay(gv[j]) * kLog2e;
             }
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) sGt[blk * DK + c1 + j] = gs[j];
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int e = tid + u * kChunkThreads;
-            if (e < C * VROWS) {
-                const int r = e / VROWS;
-                float vv[8];
-                RawVec<T, 8>::unpack(pv[u], vv);
-                if (r >= valid) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) vv[i] = 0.f;
-                }
-                store8(sV + r * LDV + (e % VROWS) * 8, vv);
-            }
-        }
-        if (tid < C) sBeta[tid] = tid < valid ? to_f(pb) : 0.f;
-        __syncthreads();
-        KDA_PROF_MARK(0);
-
-        // pass B: block tables, then one sweep over the block's 16 tokens with
-        // G the local cumulative log-decay, F = 2^G, 1/F = 2^-G
-        if (s1) {
-            float Fb[CPT], Eb[CPT];
+            float Fb[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) {
-                const int c = c1 + j;
                 float Ft[NB];
 #pragma unroll
-                for (int m = 0; m < NB; ++m) Ft[m] = fast_exp2(sGt[m * DK + c]);
+                for (int m = 0; m < NB; ++m) Ft[m] = fast_exp2(__shfl(gt[j], m * LPB + li, 64));
                 float P = 1.f, E = 1.f, F0 = 1.f;
 #pragma unroll
                 for (int m = 0; m < NB; ++m) {
@@ -333,55 +400,66 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                     if (m == blk) F0 = Ft[m];
                 }
                 Fb[j] = F0;
-                Eb[j] = E;
-                sP[blk * DK + c] = P;
-                sFt[blk * DK + c] = F0;
-                if (blk == 0) {
-                    float gam = 1.f;
+                if (s1) {
+                    const int c = c1 + j;
+                    sP[blk * DK + c] = P;
+                    sE[blk * DK + c] = E;
+                    if (blk == 0) {
+                        float gam = 1.f;
 #pragma unroll
-                    for (int m = 0; m < NB; ++m) gam *= Ft[m];
-                    sGam[c] = gam;
+                        for (int m = 0; m < NB; ++m) gam *= Ft[m];
+                        sGam[c] = gam;
 #pragma unroll
-                    for (int i2 = 2; i2 < NB; ++i2)
+                        for (int i2 = 2; i2 < NB; ++i2)
 #pragma unroll
-                        for (int j2 = 0; j2 + 2 <= i2; ++j2) {
-                            float dx = 1.f;
+                            for (int j2 = 0; j2 + 2 <= i2; ++j2) {
+                                float dx = 1.f;
 #pragma unroll
-                            for (int m = j2 + 1; m < i2; ++m) dx *= Ft[m];
-                            sDx[xidx(i2, j2) * DK + c] = dx;
-                        }
+                                for (int m = j2 + 1; m < i2; ++m) dx *= Ft[m];
+                                sDx[xidx(i2, j2) * DK + c] = dx;
+                            }
+                    }
                 }
             }
+            // one sweep over the block's 16 tokens: G = local cumulative
+            // log-decay, F = 2^G, 1/F = 2^-G
             float G[CPT];
 #pragma unroll
             for (int j = 0; j < CPT; ++j) G[j] = 0.f;
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 const int r = blk * 16 + t;
-                const bool ok = r < valid;
-                float gv[CPT], kv[CPT], qv[CPT], kf[CPT], qf[CPT], ki[CPT], kh[CPT];
+                float gv[CPT], kv[CPT], qv[CPT], kf[CPT], qf[CPT], ki[CPT], kr[CPT];
                 RawVec<T, CPT>::unpack(pg[t], gv);
                 RawVec<T, CPT>::unpack(pk[t], kv);
                 RawVec<T, CPT>::unpack(pq[t], qv);
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
-                    G[j] += ok ? clamp_log_decay(gv[j]) * kLog2e : 0.f;
+                    G[j] += clamp_log_decay(gv[j]) * kLog2e;
                     const float F = fast_exp2(G[j]);
                     const float Fi = fast_exp2(-G[j]);
-                    const float kk = ok ? kv[j] : 0.f;
-                    const float qq = ok ? qv[j] : 0.f;
-                    kf[j] = kk * F;
-                    qf[j] = qq * F;
-                    ki[j] = kk * Fi;
-                    kh[j] = (ki[j] * Fb[j]) * Eb[j];   // k e^{G_C - G_r}: both factors <= 1 in turn
+                    kf[j] = kv[j] * F;
+                    qf[j] = qv[j] * F;
+                    ki[j] = kv[j] * Fi;
+                    kr[j] = ki[j] * Fb[j];      // k e^{G_end - G_r} <= k
                 }
-                RawVec<T, CPT>::store(sKf + r * LDK + c1, kf);
-                RawVec<T, CPT>::store(sQf + r * LDK + c1, qf);
-                RawVec<T, CPT>::store(sKi + r * LDK + c1, ki);
-                RawVec<T, CPT>::store(sKh + r * LDK + c1, kh);
+                if (s1) {
+                    RawVec<T, CPT>::store(sKf + r * LDK + c1, kf);
+                    RawVec<T, CPT>::store(sQf + r * LDK + c1, qf);
+                    RawVec<T, CPT>::store(sKi + r * LDK + c1, ki);
+                    RawVec<T, CPT>::store(sKr + r * LDK + c1, kr);
+                }
             }
         }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * kChunkThreads;
+            if (e < C * VROWS) *reinterpret_cast<Raw8*>(sV + (e / VROWS) * LDV + (e % VROWS) * 8) = pv[u];
+        }
+        if (tid < C) sBeta[tid] = to_f(pb);
+        KDA_PROF_MARK(0);
         __syncthreads();
+        KDA_PROF_MARK(7);
         // the next chunk's inputs stream in while this chunk computes
         if (ci + 1 < n_chunks) {
             const int64_t rem = t_end - (tok0 + C);
@@ -390,80 +468,30 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
         KDA_PROF_MARK(1);
 
         // ================= stage 2: A_kk, A_qk tiles (MFMA) ==================
-        // Wave w computes one kind (A_kk for even w, A_qk for odd w) for row
-        // blocks {w/2, NB-1-w/2} (NB = 4) or {w/2} (NB = 2): five tiles each.
-        // Right operand: same block -> k/F; earlier block j -> (k/F) * F_j.
-        // Left operand scaled by the block totals strictly between j and i.
-        constexpr int RPW = NB >= 4 ? 2 : 1;
-        constexpr int KS = DK / KI;
-        const int kind = wave & 1;
-        const bool s2 = NB > 1 || wave < 2;
-        floatx4 accA[RPW][NB];
-#pragma unroll
-        for (int sl = 0; sl < RPW; ++sl) {
-            const int i = sl == 0 ? (wave >> 1) : NB - 1 - (wave >> 1);
-            const T* left = (kind ? sQf : sKf) + (i * 16 + lr) * LDK + KPL * lq;
-            frag la[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) la[ks] = MM::load(left + ks * KI);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                accA[sl][j] = zero4();
-                if (!s2 || j > i) continue;
-                const T* right = sKi + (j * 16 + lr) * LDK + KPL * lq;
-                const float* fr = sFt + j * DK + KPL * lq;
-                const float* dx = sDx + (i - j >= 2 ? xidx(i, j) : 0) * DK + KPL * lq;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    frag a = la[ks];
-                    if (i - j >= 2) {
-                        float av[KPL];
-                        MM::unpack(a, av);
-#pragma unroll
-                        for (int e = 0; e < KPL; ++e) av[e] *= dx[ks * KI + e];
-                        a = MM::pack(av);
-                    }
-                    frag b = MM::load(right + ks * KI);
-                    if (j < i) {
-                        float bv[KPL];
-                        MM::unpack(b, bv);
-#pragma unroll
-                        for (int e = 0; e < KPL; ++e) bv[e] *= fr[ks * KI + e];
-                        b = MM::pack(bv);
-                    }
-                    accA[sl][j] = MM::mma(a, b, accA[sl][j]);
-                }
+        {
+            floatx4 accA[kMaxS2Tiles];
+            switch (wave) {
+                case 0: stage2_compute<T, DK, NB, 0, LDK>(sKf, sQf, sKi, sKr, sDx, accA, lr, lq); break;
+                case 1: stage2_compute<T, DK, NB, 1, LDK>(sKf, sQf, sKi, sKr, sDx, accA, lr, lq); break;
+                case 2: stage2_compute<T, DK, NB, 2, LDK>(sKf, sQf, sKi, sKr, sDx, accA, lr, lq); break;
+                default: stage2_compute<T, DK, NB, 3, LDK>(sKf, sQf, sKi, sKr, sDx, accA, lr, lq); break;
             }
-        }
-        __syncthreads();   // every read of K/F done before L overwrites it
-        if (s2) {
-#pragma unroll
-            for (int sl = 0; sl < RPW; ++sl) {
-                const int i = sl == 0 ? (wave >> 1) : NB - 1 - (wave >> 1);
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    if (j > i) continue;
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const int rl = 4 * lq + ii, sl2 = lr;
-                        const int r = i * 16 + rl, s = j * 16 + sl2;
-                        if (kind == 0) {
-                            const bool keep = (j < i) || (sl2 < rl);
-                            sL[r * LDL + s] = keep ? sBeta[r] * accA[sl][j][ii] : 0.f;
-                        } else {
-                            const bool keep = (j < i) || (sl2 <= rl);
-                            sAqk[r * LDC + s] = from_f<T>(keep ? accA[sl][j][ii] : 0.f);
-                        }
-                    }
-                }
+            __syncthreads();   // every read of K/F done before L overwrites it
+            switch (wave) {
+                case 0: stage2_write<T, NB, 0, LDC, LDL>(accA, sL, sAqk, sBeta, lr, lq); break;
+                case 1: stage2_write<T, NB, 1, LDC, LDL>(accA, sL, sAqk, sBeta, lr, lq); break;
+                case 2: stage2_write<T, NB, 2, LDC, LDL>(accA, sL, sAqk, sBeta, lr, lq); break;
+                default: stage2_write<T, NB, 3, LDC, LDL>(accA, sL, sAqk, sBeta, lr, lq); break;
             }
         }
         __syncthreads();
         KDA_PROF_MARK(2);
 
-        // ================= stage 3: X = (I + L)^{-1}, M' = X diag(beta) =====
-        // Diagonal 16x16 blocks by forward substitution (wave b, lane = column),
-        // updating the remaining rows after each solved row.
+        // ================= stage 3: X = (I + L)^{-1} ===========================
+        // Diagonal 16x16 blocks by column-oriented forward substitution (wave b,
+        // lane = column of X): once x_m is final, every later row is updated
+        // with L[r][m], read from the transposed copy as a contiguous row.  X_ii
+        // is then written over the block's lower triangle (zeros above).
         if (wave < NB && lane < 16) {
             const int b0 = wave * 16;
             const int cc = lane;
@@ -471,54 +499,67 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = (r == cc) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
+            for (int m = 0; m < 15; ++m) {
+                const float4* lcol = reinterpret_cast<const float4*>(sL + (b0 + m) * LDL + b0);
+                float lv[16];
+#pragma unroll
+                for (int q4 = m / 4; q4 < 4; ++q4) {
+                    const float4 t4 = lcol[q4];
+                    lv[4 * q4] = t4.x; lv[4 * q4 + 1] = t4.y; lv[4 * q4 + 2] = t4.z; lv[4 * q4 + 3] = t4.w;
+                }
                 const float xm = acc[m];
 #pragma unroll
-                for (int r = m + 1; r < 16; ++r) acc[r] -= sL[(b0 + r) * LDL + b0 + m] * xm;
+                for (int r = m + 1; r < 16; ++r) acc[r] -= lv[r] * xm;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sL[(b0 + r) * LDL + b0 + cc] = acc[r];
         }
+        KDA_PROF_MARK(9);
         __syncthreads();
-        // Off-diagonal blocks by block rows: X_ij = -X_ii sum_{m=j}^{i-1} L_im X_mj,
-        // wave j computing the (i, j) tile with fp32 MFMA.
+        KDA_PROF_MARK(10);
+        // Off-diagonal blocks by block rows, X_ij = -X_ii sum_{m=j}^{i-1} L_im X_mj,
+        // wave j computing tile (i, j) with fp32 MFMA.  X_ij (i > j) is stored in
+        // the unused upper triangle at block position (j, i), so L stays intact.
 #pragma unroll
         for (int i = 1; i < NB; ++i) {
-            float* yw = sYb + wave * 16 * LDY;
             if (wave < i) {
+                const int j = wave;
+                float* yw = sYb + j * 16 * LDY;
                 floatx4 y = zero4();
-                for (int m = wave; m < i; ++m)
-                    y = mm16_f32(sL + (16 * i) * LDL + 16 * m, LDL, sL + (16 * m) * LDL + 16 * wave,
-                                 LDL, y, lr, lq);
+                for (int m = j; m < i; ++m) {
+                    const float* xmj = m == j ? sL + (16 * j) * LDL + 16 * j      // X_jj
+                                              : sL + (16 * j) * LDL + 16 * m;     // X_mj at (j, m)
+                    y = mm16_f32(sL + (16 * i) * LDL + 16 * m, LDL, xmj, LDL, y, lr, lq);
+                }
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) yw[(4 * lq + ii) * LDY + lr] = y[ii];
-            }
-            __syncthreads();
-            if (wave < i) {
                 const floatx4 x = mm16_f32(sL + (16 * i) * LDL + 16 * i, LDL, yw, LDY, zero4(), lr, lq);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) sL[(16 * i + 4 * lq + ii) * LDL + 16 * wave + lr] = -x[ii];
+                for (int ii = 0; ii < 4; ++ii) sL[(16 * j + 4 * lq + ii) * LDL + 16 * i + lr] = -x[ii];
             }
             __syncthreads();
         }
-        {
-            constexpr int PER = C * C / kChunkThreads > 0 ? C * C / kChunkThreads : 1;
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                const int e = tid + u * kChunkThreads;
-                if (e < C * C) {
-                    const int r = e / C, s = e % C;
-                    const float bs = sBeta[s];
-                    float val = s < r ? sL[r * LDL + s] * bs : 0.f;
-                    val = s == r ? bs : val;
-                    sM[r * LDC + s] = from_f<T>(val);
-                }
-            }
-        }
-        __syncthreads();
         KDA_PROF_MARK(3);
 
         // ================= stage 4: -W = -M'(K e^G) and Utilde = M'V ========
+        // M' = X diag(beta) is formed on the fly as the A operand: row r of
+        // block rb, columns s in block js: X in place (js == rb), at block
+        // position (js, rb) (js < rb), zero (js > rb).
+        frag am[NB][NKS];
+#pragma unroll
+        for (int rb = 0; rb < NB; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int sb = ks * KI + KPL * lq;
+                const int js = sb >> 4;
+                const int r = rb * 16 + lr;
+                const float* src = js == rb ? sL + r * LDL + sb
+                                            : sL + (js * 16 + lr) * LDL + rb * 16 + (sb & 15);
+                float xv[KPL];
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) xv[e] = js <= rb ? src[e] * sBeta[sb + e] : 0.f;
+                am[rb][ks] = MM::pack(xv);
+            }
         // W tiles: wave owns key tiles (CTW of them) for all row blocks
 #pragma unroll
         for (int jc = 0; jc < CTW; ++jc) {
@@ -527,7 +568,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb) accW[rb] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < C / KI; ++ks) {
+            for (int ks = 0; ks < NKS; ++ks) {
                 // B[k = s][n = c] = Kf[s][c] * P[block(s)][c]  (transposed read)
                 const int sb = ks * KI + KPL * lq;
                 const int c = ct * 16 + lr;
@@ -537,12 +578,8 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                 for (int e = 0; e < KPL; ++e) bv[e] = to_f(sKf[(sb + e) * LDK + c]) * pf;
                 const frag b = MM::pack(bv);
 #pragma unroll
-                for (int rb = 0; rb < NB; ++rb) {
-                    if (ks * KI < 16 * (rb + 1)) {
-                        const frag a = MM::load(sM + (rb * 16 + lr) * LDC + sb);
-                        accW[rb] = MM::mma(a, b, accW[rb]);
-                    }
-                }
+                for (int rb = 0; rb < NB; ++rb)
+                    if (ks * KI < 16 * (rb + 1)) accW[rb] = MM::mma(am[rb][ks], b, accW[rb]);
             }
 #pragma unroll
             for (int rb = 0; rb < NB; ++rb)
@@ -555,10 +592,12 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 #pragma unroll
         for (int j = 0; j < NTW; ++j) { accU[j] = zero4(); accO[j] = zero4(); }
 #pragma unroll
-        for (int ks = 0; ks < C / KI; ++ks) {
-            if (ks * KI < 16 * (rbw + 1)) {
+        for (int rb = 0; rb < NB; ++rb) {
+            if (rb != rbw) continue;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                if (ks * KI >= 16 * (rb + 1)) continue;
                 const int sb = ks * KI + KPL * lq;
-                const frag a = MM::load(sM + (rbw * 16 + lr) * LDC + sb);
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) {
                     if (ntb + WPR * j >= NT) continue;
@@ -566,11 +605,11 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                     float bv[KPL];
 #pragma unroll
                     for (int e = 0; e < KPL; ++e) bv[e] = to_f(sV[(sb + e) * LDV + n]);
-                    accU[j] = MM::mma(a, MM::pack(bv), accU[j]);
+                    accU[j] = MM::mma(am[rb][ks], MM::pack(bv), accU[j]);
                 }
             }
         }
-        __syncthreads();   // -W complete; Kf, V, M' no longer read
+        __syncthreads();   // -W complete; Kf, V, X no longer read
         KDA_PROF_MARK(4);
 
         // ================= stage 5: U += (-W) S0,  O = (Q e^G) S0 ===========
@@ -605,7 +644,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 
         // ================= stage 6: O += A_qk U;  S = diag(e^{G_C}) S + K^T U
 #pragma unroll
-        for (int ks = 0; ks < C / KI; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             if (ks * KI < 16 * (rbw + 1)) {
                 const int sb = ks * KI + KPL * lq;
                 const frag a = MM::load(sAqk + (rbw * 16 + lr) * LDC + sb);
@@ -617,14 +656,17 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                 }
             }
         }
+        {
+            const int valid = (int)((t_end - tok0) < C ? (t_end - tok0) : C);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            if (ntb + WPR * j >= NT) continue;
-            const int n = n0 + (ntb + WPR * j) * 16 + lr;
+            for (int j = 0; j < NTW; ++j) {
+                if (ntb + WPR * j >= NT) continue;
+                const int n = n0 + (ntb + WPR * j) * 16 + lr;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int r = rbw * 16 + 4 * lq + ii;
-                if (r < valid) o[((tok0 + r) * H + head) * DV + n] = from_f<T>(accO[j][ii]);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int r = rbw * 16 + 4 * lq + ii;
+                    if (r < valid) o[((tok0 + r) * H + head) * DV + n] = from_f<T>(accO[j][ii]);
+                }
             }
         }
 #pragma unroll
@@ -637,13 +679,14 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
                 for (int nt = 0; nt < NT; ++nt) S[jc][nt][ii] *= gm;
             }
 #pragma unroll
-            for (int ks = 0; ks < C / KI; ++ks) {
-                // A[m = c][k = s] = Khat[s][c]  (transposed read)
+            for (int ks = 0; ks < NKS; ++ks) {
+                // A[m = c][k = s] = (K R)[s][c] * E[block(s)][c]  (transposed read)
                 const int sb = ks * KI + KPL * lq;
                 const int c = ct * 16 + lr;
+                const float ef = sE[(sb / 16) * DK + c];
                 float av[KPL];
 #pragma unroll
-                for (int e = 0; e < KPL; ++e) av[e] = to_f(sKh[(sb + e) * LDK + c]);
+                for (int e = 0; e < KPL; ++e) av[e] = to_f(sKr[(sb + e) * LDK + c]) * ef;
                 const frag a = MM::pack(av);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)

@@ -106,6 +106,60 @@ template <> struct RawVec<__bf16, 8> : RawVecImpl<8, bf16x8, __bf16> {};
 template <> struct RawVec<float, 2> : RawVecImpl<2, floatx2, float> {};
 template <> struct RawVec<float, 8> : RawVecImpl<8, floatx8, float> {};
 
+// ---- raw buffer loads ---------------------------------------------------------
+// A buffer resource covers [base, base + bytes); loads whose offset falls
+// outside return zero, which is how rows past the end of a sequence are padded.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped) buffer, gfx9 family
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferWord3);
+}
+
+template <typename T, int N>
+struct BufLoad;
+template <>
+struct BufLoad<__bf16, 1> {
+    static __device__ __forceinline__ __bf16 load(rsrc_t r, int off) {
+        return __builtin_bit_cast(__bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<__bf16, 2> {
+    static __device__ __forceinline__ bf16x2 load(rsrc_t r, int off) {
+        return __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<__bf16, 8> {
+    static __device__ __forceinline__ bf16x8 load(rsrc_t r, int off) {
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<float, 1> {
+    static __device__ __forceinline__ float load(rsrc_t r, int off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<float, 2> {
+    static __device__ __forceinline__ floatx2 load(rsrc_t r, int off) {
+        return __builtin_bit_cast(floatx2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<float, 8> {
+    // Whole-vector casts only: assembling the result from per-element casts of
+    // the two 128-bit loads has been seen to compile into 32-bit loads.
+    static __device__ __forceinline__ floatx8 load(rsrc_t r, int off) {
+        const floatx4 a = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        const floatx4 b = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
 // ---- math --------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
