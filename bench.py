@@ -86,13 +86,13 @@ def decode_bytes(B, H, D, es=2):
             + P * 4 * 4)                 # conv weights
 
 
-def cpu_baseline(inp, spec, T_s):
-    """Oracle on the first T_s tokens of as many heads as it has threads."""
+def cpu_baseline(inp, spec, T_s, H_s):
+    """Oracle on the first T_s tokens of the first H_s heads (all its threads)."""
     import numpy as np
     import torch
     from oracle import c_oracle
     nthr = c_oracle.num_threads()
-    H_s = min(nthr, spec.H)
+    H_s = min(H_s, spec.H)
     heads = list(range(H_s))
     H, D = spec.H, spec.D
     cols = []
@@ -122,9 +122,13 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=64)
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--cpu-heads", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 counter passes: a few chunk-kernel launches "
+                         "at T=65536 plus a plain copy kernel of known size for calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA mixer here is a single-GPU library "
@@ -166,6 +170,23 @@ def main():
         kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
         if events:
             events[3].record(stream)
+
+    if args.counters:
+        # the recurrence kernel alone (after one conv pass to produce its
+        # inputs), then an elementwise copy of 2 GiB in and 2 GiB out, whose
+        # byte counters calibrate the recurrence's
+        kda.kda_conv(x, w, y_qkv, 1, N, H, D, stream=stream)
+        for _ in range(3):
+            kda.kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD,
+                                  g, beta, o, 1, N, H, D, D, chunk=C, final_state=sT,
+                                  stream=stream)
+        src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("counter run done: 3 chunk launches, 3 copies of 2 GiB")
+        return
 
     for _ in range(args.warmup):
         step()
@@ -258,7 +279,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_tokens)
+        result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_tokens, args.cpu_heads)
         log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
     print(json.dumps(result), flush=True)
 

@@ -1,0 +1,116 @@
+"""Summarise rocprofv3 output of bench.py into profiles/.
+
+Inputs (CSV files written by the commands recorded in the summaries):
+  --trace  <dir>/bench_kernel_stats.csv   from
+           rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- \
+               python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
+  --fetch  <dir>/fetch_counter_collection.csv from
+           rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters
+  --write  <dir>/write_counter_collection.csv from
+           rocprofv3 --pmc WRITE_SIZE -T -f csv -d <dir> -o write -- python3 bench.py --counters
+
+Writes profiles/chunk_prefill_T65536_kernel_stats.txt and
+profiles/chunk_prefill_T65536_traffic.json.  The byte counters (KiB per
+dispatch) are scaled by what the same counter reads for bench.py's copy
+kernel of known size (2 GiB read, 2 GiB written); the JSON records the hash
+of the chunk-kernel sources so bench.py can tell whether it is current.
+"""
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+COPY_BYTES = 2 * 1024 ** 3
+CHUNK_TAG = "chunk_kernel"
+COPY_TAG = "vectorized_elementwise_kernel"
+
+
+def per_dispatch(path, counter):
+    vals = {}
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = r["Dispatch_Id"]
+        vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(names[d], vals[d]) for d in sorted(vals, key=int)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    args = ap.parse_args()
+    import bench
+
+    # kernel-trace statistics
+    rows = list(csv.DictReader(open(args.trace)))
+    lines = ["# rocprofv3 kernel statistics of one bench.py run (prefill T=65536, H=96, D=128,",
+             "# bf16 I/O; decode B=256 x 64 steps), MI355X",
+             "# command: rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- "
+             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+             f"{'kernel':60s} {'calls':>6s} {'avg_ms':>10s} {'min_ms':>10s} {'max_ms':>10s} {'pct':>6s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e6:10.4f} "
+                     f"{float(r['MinNs'])/1e6:10.4f} {float(r['MaxNs'])/1e6:10.4f} "
+                     f"{float(r['Percentage']):6.2f}")
+    chunk_avg = [float(r["AverageNs"]) / 1e6 for r in rows if CHUNK_TAG in r["Name"]]
+
+    # byte counters
+    fetch = per_dispatch(args.fetch, "FETCH_SIZE")
+    write = per_dispatch(args.write, "WRITE_SIZE")
+    f_chunk = [v for n, v in fetch if CHUNK_TAG in n]
+    w_chunk = [v for n, v in write if CHUNK_TAG in n]
+    # the copy dispatches are the last three elementwise kernels of the run
+    f_copy = [v for n, v in fetch if COPY_TAG in n][-3:]
+    w_copy = [v for n, v in write if COPY_TAG in n][-3:]
+    f_scale = COPY_BYTES / (statistics.mean(f_copy) * 1024)
+    w_scale = COPY_BYTES / (statistics.mean(w_copy) * 1024)
+    fb = statistics.mean(f_chunk) * 1024 * f_scale
+    wb = statistics.mean(w_chunk) * 1024 * w_scale
+    algo = bench.prefill_bytes(65536, 96, 128, 1)["chunk"]
+    rec = {
+        "kernel": "chunk_kernel<bf16, DK=128, DV slice=64, chunk=64> (kda_chunk_prefill), "
+                  "T=65536, H=96",
+        "source_sha256": bench.chunk_source_hash(),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters",
+            "rocprofv3 --pmc WRITE_SIZE -T -f csv -d <dir> -o write -- python3 bench.py --counters",
+        ],
+        "fetch_kib_per_dispatch": statistics.mean(f_chunk),
+        "write_kib_per_dispatch": statistics.mean(w_chunk),
+        "copy_calibration": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                             "fetch_kib": statistics.mean(f_copy),
+                             "write_kib": statistics.mean(w_copy),
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "fetch_bytes_per_launch": fb,
+        "write_bytes_per_launch": wb,
+        "traffic_bytes_per_launch": fb + wb,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": (fb + wb) / algo,
+        "kernel_trace_avg_ms": chunk_avg[0] if chunk_avg else None,
+    }
+    lines += ["",
+              "# HBM bytes of the chunk kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+              "# scaled by the same counters on a copy kernel of 2 GiB in / 2 GiB out:",
+              f"#   FETCH_SIZE {rec['fetch_kib_per_dispatch']:.0f} KiB x {f_scale:.3f} = {fb/1e9:.3f} GB",
+              f"#   WRITE_SIZE {rec['write_kib_per_dispatch']:.0f} KiB x {w_scale:.3f} = {wb/1e9:.3f} GB",
+              f"#   traffic {(fb+wb)/1e9:.3f} GB vs algorithmic {algo/1e9:.3f} GB "
+              f"({rec['traffic_over_algorithmic']:.3f}x)"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "chunk_prefill_T65536_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(bench.TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=2)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
