@@ -21,7 +21,10 @@ namespace {
 
 constexpr int kConvThreads = 256;
 constexpr int kConvChannels = kConvThreads * 8;
-constexpr int kTile = 32;
+// tokens per thread: all of a tile's inputs (plus the 3-token halo) are loaded
+// before any arithmetic, so a thread keeps TT + 3 16-byte loads in flight
+template <typename T>
+struct ConvTile { static constexpr int TT = sizeof(T) == 2 ? 16 : 8; };
 
 struct SeqRange {
     int s;
@@ -81,10 +84,12 @@ __global__ void __launch_bounds__(kConvThreads)
 conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ y,
             const T* __restrict__ state_in, const int32_t* __restrict__ cu, int num_seqs,
             int T_len, int64_t N, int P, int HD, float l2_eps) {
+    constexpr int TT = ConvTile<T>::TT;
+    using Raw8 = typename RawVec<T, 8>::type;
     const int c0 = blockIdx.y * kConvChannels + threadIdx.x * 8;
     const bool active = c0 < P;
-    const int64_t t0 = (int64_t)blockIdx.x * kTile;
-    const int64_t t1 = t0 + kTile < N ? t0 + kTile : N;
+    const int64_t t0 = (int64_t)blockIdx.x * TT;
+    const int64_t t1 = t0 + TT < N ? t0 + TT : N;
     const bool is_qk = c0 < 2 * HD;   // uniform over the D/8 lanes of a head
 
     float wt[8][4];
@@ -94,6 +99,50 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
         for (int i = 0; i < 4; ++i) wt[e][i] = active ? w[(c0 + e) * 4 + i] : 0.f;
 
     SeqRange sr = find_seq(cu, num_seqs, T_len, t0);
+
+    // Fast path (uniform over the block): the tile and its halo lie inside one
+    // sequence, so every window reads plain inputs.
+    if (sr.start <= t0 - 3 && sr.end >= t0 + TT) {
+        const int cl = active ? c0 : 0;
+        Raw8 raw[TT + 3];
+#pragma unroll
+        for (int j = 0; j < TT + 3; ++j)
+            raw[j] = *reinterpret_cast<const Raw8*>(x + (t0 - 3 + j) * P + cl);
+        float win[8][3];
+        {
+            float v0[8], v1[8], v2[8];
+            RawVec<T, 8>::unpack(raw[0], v0);
+            RawVec<T, 8>::unpack(raw[1], v1);
+            RawVec<T, 8>::unpack(raw[2], v2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { win[e][0] = v0[e]; win[e][1] = v1[e]; win[e][2] = v2[e]; }
+        }
+#pragma unroll
+        for (int j = 0; j < TT; ++j) {
+            float xv[8], out[8];
+            RawVec<T, 8>::unpack(raw[j + 3], xv);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pre = wt[e][0] * win[e][0] + wt[e][1] * win[e][1] +
+                                  wt[e][2] * win[e][2] + wt[e][3] * xv[e];
+                out[e] = siluf_(pre);
+                ss += out[e] * out[e];
+                win[e][0] = win[e][1];
+                win[e][1] = win[e][2];
+                win[e][2] = xv[e];
+            }
+            ss = group_sum<D / 8>(ss);
+            if (is_qk) {
+                const float inv = rsqrt_nr(ss + l2_eps);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] *= inv;
+            }
+            if (active) store8_nt(y + (t0 + j) * P + c0, out);
+        }
+        return;
+    }
+
     // window: win[e][0] = x_{t-3}, win[e][1] = x_{t-2}, win[e][2] = x_{t-1}
     float win[8][3];
     if (active) {
@@ -155,7 +204,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
 #pragma unroll
             for (int e = 0; e < 8; ++e) out[e] *= inv;
         }
-        if (active) store8(y + t * P + c0, out);
+        if (active) store8_nt(y + t * P + c0, out);
     }
 }
 
@@ -200,7 +249,8 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
     const int P = 3 * H * D;
     const unsigned cblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
     if (N > 0) {
-        const unsigned tiles = (unsigned)((N + kTile - 1) / kTile);
+        constexpr int TT = ConvTile<T>::TT;
+        const unsigned tiles = (unsigned)((N + TT - 1) / TT);
         hipLaunchKernelGGL((conv_kernel<T, D>), dim3(tiles, cblocks), dim3(kConvThreads), 0, s,
                            (const T*)x, w, (T*)y, (const T*)state_in, cu, num_seqs, T_len, N, P,
                            H * D, l2_eps);

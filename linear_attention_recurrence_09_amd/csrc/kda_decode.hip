@@ -8,7 +8,8 @@
 // read S^T q.
 //
 // One workgroup per (sequence, head).  The state is one streaming pass: each
-// thread loads its 16 (D = 128) float4's of S, decays them, accumulates
+// of 256 threads loads its 16 (D = 128) float4 of S (non-temporal: the state
+// is streamed once per step), decays them, accumulates
 // Sbar^T k and Sbar^T q for its 4 columns, the column sums are reduced across
 // row groups, and the same registers are updated and stored.  The read uses
 // o = Sbar^T q + beta (k . q) e, which equals S_t^T q.  HBM traffic is one read
@@ -20,7 +21,30 @@ namespace kda {
 
 namespace {
 
-constexpr int kDecThreads = 256;
+#ifndef KDA_DECODE_THREADS
+#define KDA_DECODE_THREADS 256
+#endif
+#ifndef KDA_DECODE_NONTEMPORAL
+#define KDA_DECODE_NONTEMPORAL 1
+#endif
+constexpr int kDecThreads = KDA_DECODE_THREADS;
+
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+#if KDA_DECODE_NONTEMPORAL
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+template <typename V>
+__device__ __forceinline__ void stream_store(V v, V* p) {
+#if KDA_DECODE_NONTEMPORAL
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads)
@@ -48,10 +72,10 @@ decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_stat
     const int cg = tid % CG;
     const int rg = tid / CG;
     float* Sbh = state + (int64_t)bh * D * D;
-    float4 sv[RPT];
+    floatx4 sv[RPT];   // streamed once: non-temporal loads and stores
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
-        sv[j] = *reinterpret_cast<const float4*>(Sbh + (rg + R * j) * D + 4 * cg);
+        sv[j] = stream_load(reinterpret_cast<const floatx4*>(Sbh + (rg + R * j) * D + 4 * cg));
 
     // ---- conv window + SiLU + L2 -------------------------------------------
     float y0 = 0.f, y1 = 0.f;
@@ -104,10 +128,10 @@ decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_stat
     for (int j = 0; j < RPT; ++j) {
         const int i = rg + R * j;
         const float a = sa[i];
-        sv[j].x *= a; sv[j].y *= a; sv[j].z *= a; sv[j].w *= a;
+        sv[j] *= a;
         const float ki = su[D + i], qi = su[i];
-        ak.x += ki * sv[j].x; ak.y += ki * sv[j].y; ak.z += ki * sv[j].z; ak.w += ki * sv[j].w;
-        aq.x += qi * sv[j].x; aq.y += qi * sv[j].y; aq.z += qi * sv[j].z; aq.w += qi * sv[j].w;
+        ak.x += ki * sv[j][0]; ak.y += ki * sv[j][1]; ak.z += ki * sv[j][2]; ak.w += ki * sv[j][3];
+        aq.x += qi * sv[j][0]; aq.y += qi * sv[j][1]; aq.z += qi * sv[j][2]; aq.w += qi * sv[j][3];
     }
     // row groups inside a wave differ in lane bits >= log2(CG)
 #pragma unroll
@@ -148,9 +172,9 @@ decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_stat
     for (int j = 0; j < RPT; ++j) {
         const int i = rg + R * j;
         const float bk = bt * su[D + i];
-        float4 r = sv[j];
-        r.x += bk * ev[0]; r.y += bk * ev[1]; r.z += bk * ev[2]; r.w += bk * ev[3];
-        *reinterpret_cast<float4*>(Sbh + i * D + 4 * cg) = r;
+        floatx4 r = sv[j];
+        r[0] += bk * ev[0]; r[1] += bk * ev[1]; r[2] += bk * ev[2]; r[3] += bk * ev[3];
+        stream_store(r, reinterpret_cast<floatx4*>(Sbh + i * D + 4 * cg));
     }
 }
 

@@ -50,6 +50,31 @@ __device__ __forceinline__ void store8(__bf16* p, const float v[8]) {
     *reinterpret_cast<bf16x8*>(p) = a;
 }
 
+// Non-temporal variants for data streamed once (no reuse through the caches).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
+    const floatx4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<floatx4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<floatx4*>(p + 4));
+}
+__device__ __forceinline__ void store8_nt(__bf16* p, const float v[8]) {
+    bf16x8 a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (__bf16)v[i];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, a), reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void load8_nt(const float* p, float v[8]) {
+    const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void load8_nt(const __bf16* p, float v[8]) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+}
+
 // ---- 2-wide I/O --------------------------------------------------------------
 __device__ __forceinline__ void load2(const float* p, float& a, float& b) {
     const float2 t = *reinterpret_cast<const float2*>(p);

@@ -37,8 +37,8 @@ gated_norm_kernel(const T* o, const T* __restrict__ gate,
     for (int j = 0; j < kNormRowsPerThread; ++j) {
         const int64_t r = row0 + (int64_t)j * RPP + row_in_pass;
         if (r < rows) {
-            load8(o + r * D + d0, ov[j]);
-            load8(gate + r * D + d0, zv[j]);
+            load8_nt(o + r * D + d0, ov[j]);
+            load8_nt(gate + r * D + d0, zv[j]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) { ov[j][e] = 0.f; zv[j][e] = 0.f; }
@@ -55,7 +55,7 @@ gated_norm_kernel(const T* o, const T* __restrict__ gate,
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] = ov[j][e] * inv * wv[e] * sigmoidf_(zv[j][e]);
         const int64_t r = row0 + (int64_t)j * RPP + row_in_pass;
-        if (r < rows) store8(y + r * D + d0, out);
+        if (r < rows) store8_nt(y + r * D + d0, out);
     }
 }
 
