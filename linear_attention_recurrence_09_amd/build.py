@@ -18,7 +18,8 @@ OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kda_api.cpp", "kda_norm.hip", "kda_conv.hip", "kda_decode.hip", "kda_chunk.hip"]
+SOURCES = ["kda_api.cpp", "kda_norm.hip", "kda_conv.hip", "kda_decode.hip", "kda_chunk.hip",
+           "kda_chunk_pipe.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

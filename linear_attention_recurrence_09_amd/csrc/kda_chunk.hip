@@ -732,15 +732,21 @@ hipError_t launch_chunk_t(const void* q, const void* k, const void* v, int64_t s
 
 }  // namespace
 
-// Variants compiled: bf16 with chunk 32/64 and value slices of 64/128 columns;
+// Variants compiled here: bf16 with chunk 32/64 and value slices of 64/128 columns;
 // fp32 with chunk 16/32/64 and 32-column slices (fp32 DK = 128 at chunk 64
 // exceeds the LDS budget).
 ChunkPlan plan_chunk(int dtype, int DK, int DV, int chunk, int64_t n_chains) {
-    ChunkPlan p{0, 0, false};
+    ChunkPlan p{0, 0, false, false};
     if (chunk != 16 && chunk != 32 && chunk != 64) return p;
     p.nb = chunk / 16;
     if (dtype == 1) {
-        if (chunk == 16) return p;
+        if (chunk == 16) {
+            // producer / consumer kernel, 64 value columns per workgroup
+            p.dvs = 64;
+            p.pipe = true;
+            p.ok = true;
+            return p;
+        }
         // fewer chains than CUs: split the value columns to fill the chip
         p.dvs = (DV == 128 && n_chains < 256) ? 64 : DV;
         p.ok = true;
@@ -761,6 +767,8 @@ hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, con
                         int64_t stride, const void* g, const void* beta, void* o,
                         const float* s0, float* sT, const int32_t* cu, int num_seqs, int T,
                         int H, int DK, int DV, int dtype, hipStream_t s) {
+    if (plan.pipe)
+        return launch_chunk_pipe(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H, DK, DV, s);
     if (dtype == 1) {
         KDA_CHUNK_CASE(__bf16, 128, 128, 4)
         KDA_CHUNK_CASE(__bf16, 128, 64, 4)

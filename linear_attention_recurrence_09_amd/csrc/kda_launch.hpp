@@ -23,8 +23,15 @@ struct ChunkPlan {
     int nb;       // 16-token blocks per chunk (chunk = 16 * nb)
     int dvs;      // value columns per workgroup (DV / dvs workgroups per head)
     bool ok;      // false when no compiled variant fits the request
+    bool pipe;    // bf16, 16-token chunks: producer / consumer wave kernel
 };
 ChunkPlan plan_chunk(int dtype, int DK, int DV, int chunk, int64_t n_chains);
+
+// bf16, 16-token chunks, 64 value columns per workgroup (kda_chunk_pipe.hip).
+hipError_t launch_chunk_pipe(const void* q, const void* k, const void* v, int64_t stride,
+                             const void* g, const void* beta, void* o, const float* s0,
+                             float* sT, const int32_t* cu, int num_seqs, int T, int H, int DK,
+                             int DV, hipStream_t s);
 
 hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, const void* v,
                         int64_t stride, const void* g, const void* beta, void* o,

@@ -76,7 +76,8 @@ def test_chunk_argument_checks(L):
     assert chunk(L, q=None) == INVALID
     assert chunk(L, DK=96) == UNSUPPORTED
     assert chunk(L, C=48) == UNSUPPORTED
-    assert chunk(L, C=16) == UNSUPPORTED                     # bf16 needs chunk >= 32
+    assert chunk(L, C=8) == UNSUPPORTED
+    assert chunk(L, C=16) not in (INVALID, UNSUPPORTED)      # bf16 chunk 16: passes the checks
     assert chunk(L, dt=0, C=64) == UNSUPPORTED               # fp32 with DK=128 at chunk 64
     assert chunk(L, stride=100) == INVALID
     assert chunk(L, o=A + 64) == INVALID                     # o overlaps q/k/v

@@ -142,6 +142,13 @@ CHUNK_CASES = [
     ("bf16", 64, 4, [190], False, 64, True, -0.05),
     ("bf16", 128, 2, [0, 5, 64, 130, 1, 0, 65], True, 64, True, -0.05),
     ("bf16", 128, 2, [100, 100, 100], False, 64, False, -5.0),
+    # 16-token chunks: producer / consumer kernel (ring of 6 LDS slots)
+    ("bf16", 128, 4, [300], False, 16, True, -5.0),
+    ("bf16", 128, 4, [300], False, 16, True, -0.05),
+    ("bf16", 64, 4, [190], False, 16, True, -0.05),
+    ("bf16", 128, 2, [0, 5, 64, 130, 1, 0, 65], True, 16, True, -0.05),
+    ("bf16", 128, 2, [100, 100, 100], False, 16, False, -5.0),
+    ("bf16", 128, 2, [2000], False, 16, True, -0.05),
     # 32 sequences x 8 heads = 256 chains: takes the full 128-column slices
     ("bf16", 128, 8, [int(v) for v in np.random.default_rng(5).integers(1, 150, 32)], True, 64,
      True, -0.05),
@@ -199,3 +206,44 @@ def test_chunk_prefill(case):
                               o2, B, T, H, D, D, **kw)
         torch.cuda.synchronize()
         assert torch.equal(o2, o) and torch.equal(st, sT)
+
+
+@pytest.mark.gpu
+def test_chunk16_repeatable():
+    """The 16-token kernel hands LDS slots between waves through counters; any
+    ordering fault shows up as outputs that differ between identical calls.
+    Many heads and sequence lengths that wrap the slot ring several times."""
+    H, D, lengths = 16, 128, [700, 333, 1000]
+    N, S = sum(lengths), len(lengths)
+    HD = H * D
+    dt = torch.bfloat16
+    qkv = torch.empty((N, 3 * HD), dtype=dt, device="cuda")
+    qkv[:, :HD] = _unit_rows((N, H, D), 40, dt).reshape(N, HD)
+    qkv[:, HD:2 * HD] = _unit_rows((N, H, D), 41, dt).reshape(N, HD)
+    qkv[:, 2 * HD:] = _randn((N, HD), 42, dt)
+    g = (-0.05 * torch.rand((N, H, D), generator=_gen(43), device="cuda")).to(dt)
+    beta = torch.sigmoid(torch.randn((N, H), generator=_gen(44), device="cuda")).to(dt)
+    S0 = _randn((S, H, D, D), 45, torch.float32, 0.1)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
+    outs = []
+    for rep in range(6):
+        o = torch.full((N, H, D), float(rep), dtype=dt, device="cuda")
+        sT = torch.full((S, H, D, D), float(rep), dtype=torch.float32, device="cuda")
+        kda.kda_chunk_prefill(qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:], 3 * HD, g, beta, o,
+                              1, N, H, D, D, chunk=16, initial_state=S0, final_state=sT,
+                              cu_seqlens=cu, num_seqs=S)
+        torch.cuda.synchronize()
+        outs.append((o, sT))
+    for rep in range(1, 6):
+        assert torch.equal(outs[rep][0], outs[0][0]), f"o differs between calls (call {rep})"
+        assert torch.equal(outs[rep][1], outs[0][1]), f"final state differs between calls (call {rep})"
+    # one head against the oracle
+    f = lambda t: t.detach().double().cpu().numpy()
+    h, s = 5, 2
+    t0, t1 = int(cu[s]), int(cu[s + 1])
+    o_ref, S_ref = c_oracle.gated_delta_rule(
+        f(qkv[t0:t1, h * D:(h + 1) * D]), f(qkv[t0:t1, HD + h * D:HD + (h + 1) * D]),
+        f(qkv[t0:t1, 2 * HD + h * D:2 * HD + (h + 1) * D]), f(g[t0:t1, h]), f(beta[t0:t1, h]),
+        f(S0[s, h]))
+    assert report("o", f(outs[0][0][t0:t1, h]), o_ref, TOL["bf16"]) <= TOL["bf16"]
+    assert report("S_T", f(outs[0][1][s, h]), S_ref, TOL["bf16"]) <= TOL["bf16"]
