@@ -39,8 +39,43 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
+// Optional phase timing (profiling builds define KDA_PIPE_PROFILE and the
+// array): lane 0 of producer wave 0 and of consumer wave 0 in workgroup 0
+// record the cycles spent in each phase.
 #ifdef KDA_PIPE_PROFILE
 extern __device__ unsigned long long kda_pipe_cycles[16];
+#define PIPE_PROF_INIT()                                           \
+    unsigned long long pt_ = __builtin_readcyclecounter();        \
+    unsigned long long pa_[8] = {}
+#define PIPE_PROF_MARK(i)                                          \
+    do {                                                           \
+        const unsigned long long t_ = __builtin_readcyclecounter(); \
+        pa_[i] += t_ - pt_;                                        \
+        pt_ = t_;                                                  \
+    } while (0)
+#define PIPE_PROF_FLUSH(base, cond)                                            \
+    do {                                                                       \
+        if (blockIdx.x == 0 && (cond) && lane == 0)                            \
+            for (int i_ = 0; i_ < 8; ++i_) kda_pipe_cycles[(base) + i_] = pa_[i_]; \
+    } while (0)
+#define PIPE_PROF_FLUSH_CONSUMER(w)                                            \
+    do {                                                                       \
+        if (blockIdx.x == 0 && lane == 0) {                                    \
+            kda_pipe_cycles[8 + (w)] = pa_[0];                                 \
+            kda_pipe_cycles[12 + (w)] = pa_[1] + pa_[2];                       \
+        }                                                                      \
+    } while (0)
+#define PIPE_PROF_VMWAIT(i)                                                    \
+    do {                                                                       \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                       \
+        PIPE_PROF_MARK(i);                                                     \
+    } while (0)
+#else
+#define PIPE_PROF_INIT() do {} while (0)
+#define PIPE_PROF_MARK(i) do {} while (0)
+#define PIPE_PROF_FLUSH(base, cond) do {} while (0)
+#define PIPE_PROF_FLUSH_CONSUMER(w) do {} while (0)
+#define PIPE_PROF_VMWAIT(i) do {} while (0)
 #endif
 
 namespace kda {
@@ -51,15 +86,21 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16v4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
 
-constexpr int kNP = 4;                 // producer waves
-constexpr int kRing = 6;               // LDS slots
+constexpr int kNP = 8;                 // producer waves (two per SIMD)
+constexpr int kRing = 8;               // LDS slots
 constexpr int kSpinLimit = 1 << 17;    // polls (about 128 cycles each) before giving up
+#ifndef KDA_PIPE_SLEEP
+#define KDA_PIPE_SLEEP 2                // s_sleep argument between polls (64 cycles each)
+#endif
+#ifndef KDA_PIPE_CONSUMER_PRIO
+#define KDA_PIPE_CONSUMER_PRIO 0        // wave priority of the consumer waves (0-3)
+#endif
 
 template <int DK, int DVS>
 struct PipeCfg {
     static constexpr int NC = DVS / 16;                 // consumer waves
     static constexpr int THREADS = 64 * (NC + kNP);
-    static constexpr int CPL = DK / 64;                 // channels per producer lane
+    static constexpr int CPT = DK / 16;                 // channels per producer lane (4 tokens each)
     static constexpr int NKS = DK / 32;                 // 16x16x32 steps over the key channels
     static constexpr int NKT = DK / 16;                 // 16-row key tiles of the state
     // Row pitches (bytes).  Tiles read 16 B per lane along a row get a 16 B
@@ -67,21 +108,23 @@ struct PipeCfg {
     // read get 32 B (8 banks apart).
     static constexpr int PK = DK * 2 + 16;
     static constexpr int PH = DK * 2 + 32;
-    static constexpr int PV = DVS * 2 + 32;
+    // one ring slot (a chunk handed to the consumers)
     static constexpr int O_KT = 0;                      // K e^G       (permuted channels)
     static constexpr int O_QT = O_KT + 16 * PK;         // Q e^G       (permuted channels)
-    static constexpr int O_KI = O_QT + 16 * PK;         // K e^-G      (permuted channels)
-    static constexpr int O_KH = O_KI + 16 * PK;         // K e^{G15-G} (natural order)
-    static constexpr int O_V = O_KH + 16 * PH;          // V slice
-    static constexpr int O_MP = O_V + 16 * PV;          // M' as 16x16x16 A operands
+    static constexpr int O_KH = O_QT + 16 * PK;         // K e^{G15-G} (natural order)
+    static constexpr int O_MP = O_KH + 16 * PH;         // M' as 16x16x16 A operands
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    static constexpr int BYTES = kRing * SLOT;
+    // K e^-G (permuted channels): read only by the producer that wrote it, so
+    // each producer wave has one private tile after the ring
+    static constexpr int O_KI = kRing * SLOT;
+    static constexpr int BYTES = O_KI + kNP * 16 * PK;
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
     static_assert(BYTES <= 160 * 1024 - 256, "LDS budget");
+    static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
 };
 
 // Position of channel c inside its 32-channel group in the permuted tiles:
@@ -116,17 +159,60 @@ __device__ __forceinline__ bf16v4 lds_read_tr(const char* p) {
 // Lane n of every 16-lane row, broadcast to the whole row.
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 0x150 + N, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              0x150 + N, 0xF, 0xF, true));
 }
-// Row G (lanes 16G .. 16G+15) copied to all four rows, lane order kept.
-template <int G>
-__device__ __forceinline__ float rows_from(float x) {
+// The value of row g (lanes 16g .. 16g+15) in every row, for g = 0..3, lane
+// order kept: two gfx950 cross-row swaps produce all four broadcasts.
+__device__ __forceinline__ void all_rows(float x, float (&out)[4]) {
     const int xi = __builtin_bit_cast(int, x);
-    const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-    const int a = (G & 1) ? (int)p16[1] : (int)p16[0];      // rows {G&1, G&1, 2+(G&1), 2+(G&1)}
-    const auto p32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-    return __builtin_bit_cast(float, (G & 2) ? (int)p32[1] : (int)p32[0]);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);   // rows 0022 / 1133
+    const auto e = __builtin_amdgcn_permlane32_swap((int)p16[0], (int)p16[0], false, false);
+    const auto o = __builtin_amdgcn_permlane32_swap((int)p16[1], (int)p16[1], false, false);
+    out[0] = __builtin_bit_cast(float, (int)e[0]);
+    out[1] = __builtin_bit_cast(float, (int)o[0]);
+    out[2] = __builtin_bit_cast(float, (int)e[1]);
+    out[3] = __builtin_bit_cast(float, (int)o[1]);
+}
+// The value of the neighbouring row (row r ^ 1).
+__device__ __forceinline__ float pair_row(float x, int row) {
+    const int xi = __builtin_bit_cast(int, x);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);   // rows 0022 / 1133
+    return __builtin_bit_cast(float, (row & 1) ? (int)p16[0] : (int)p16[1]);
+}
+
+// y += (lane M of the row's n) * m, one v_fmac_f32 with a DPP row broadcast
+// on its first source.  The broadcast operand must not be written by a VALU
+// instruction in the two instructions before (see back_subst).
+template <int M>
+__device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(y)
+                 : "v"(n), "v"(m), "i"(M));
+}
+
+template <int M>
+__device__ __forceinline__ void back_subst_steps(float (&y)[16], const float (&np)[16]) {
+    if constexpr (M >= 1) {
+#pragma unroll
+        for (int r = 0; r < M; ++r) fmac_bcast<M>(y[r], np[r], y[M]);
+        back_subst_steps<M - 1>(y, np);
+    }
+}
+
+// Back substitution for Y = (I + N)^{-1}, N strictly upper triangular, in a
+// column layout replicated over the four rows: lane c of every row holds
+// column c of -N in np[0..15] and builds column c of Y - I in y[0..15].
+// With y started at np, Y - I = -N + (-N)(Y - I) is solved column-oriented:
+// entry M of y is final once the entries above it are done, and it updates
+// every row r < M with -N[r][M], taken from lane M of the row.  np is complete
+// before the first broadcast read (the s_nop consumes it and adds the DPP read
+// wait states).
+__device__ __forceinline__ void back_subst(float (&y)[16], const float (&np)[16]) {
+    asm volatile("s_nop 1" ::"v"(np[0]), "v"(np[1]), "v"(np[2]), "v"(np[3]), "v"(np[4]),
+                 "v"(np[5]), "v"(np[6]), "v"(np[7]), "v"(np[8]), "v"(np[9]), "v"(np[10]),
+                 "v"(np[11]), "v"(np[12]), "v"(np[13]), "v"(np[14]));
+    back_subst_steps<15>(y, np);
 }
 
 // S[KT..] <- diag(e^{G_15}) S + Kh^T U for the key tiles KT .. NKT-1.  Row i
@@ -167,7 +253,7 @@ __device__ __forceinline__ bool wait_at_least(int* f, int target, int* stop) {
             __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(KDA_PIPE_SLEEP);
     }
     return true;
 }
@@ -180,8 +266,8 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                   float* sT, const int32_t* __restrict__ cu, int num_seqs, int T_len, int H,
                   int DV, int nsplit) {
     using Cfg = PipeCfg<DK, DVS>;
-    constexpr int NC = Cfg::NC, CPL = Cfg::CPL, NKS = Cfg::NKS, NKT = Cfg::NKT;
-    constexpr int PK = Cfg::PK, PH = Cfg::PH, PV = Cfg::PV, SLOT = Cfg::SLOT;
+    constexpr int NC = Cfg::NC, NKS = Cfg::NKS, NKT = Cfg::NKT;
+    constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
     __shared__ int flags[2 * kRing + 1];   // ready[kRing], released[kRing], stop
@@ -224,13 +310,19 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
     if (wave >= NC) {
         // ===================== producer wave =================================
+        // Stage-1 lane layout: lane (row tg, column cg) holds channels
+        // cg*CPT .. cg*CPT+CPT-1 of tokens 4tg .. 4tg+3 -- one wide load per
+        // token and tensor.  Decay products run serially over the lane's four
+        // tokens; the products over the other rows come from cross-row swaps.
         const int pw = wave - NC;
-        const int c0 = lane * CPL;                 // this lane's channels
-        using RawC = typename RawVec<__bf16, CPL>::type;
-        constexpr int VL = DVS / 32;               // 16 B pieces of V per lane
-        RawC rg[16], rk[16], rq[16];
-        u32x4 rv[VL];
-        __bf16 rbl, rb4[4];
+        constexpr int CPT = Cfg::CPT;
+        const int tg = lane >> 4, cg = lane & 15;
+        const int c0 = cg * CPT;
+        using RawT = typename RawVec<__bf16, CPT>::type;
+        RawT rg[4], rk[4], rq[4];
+        // beta as zero-extended 32-bit words: 16-bit values would be packed in
+        // pairs right after the loads, which makes the wave wait for them
+        uint32_t rbl, rb4[4];
         const int g_row = H * DK * 2, kv_row = (int)(stride * 2), b_row = H * 2;
         auto issue_loads = [&](int64_t ci) {
             const int64_t t0 = t_begin + ci * 16;
@@ -240,97 +332,114 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const rsrc_t r_k = make_rsrc(k + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
             const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                rg[t] = BufLoad<__bf16, CPL>::load(r_g, t * g_row + c0 * 2);
-                rk[t] = BufLoad<__bf16, CPL>::load(r_k, t * kv_row + c0 * 2);
-                rq[t] = BufLoad<__bf16, CPL>::load(r_q, t * kv_row + c0 * 2);
-            }
-            const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
-#pragma unroll
-            for (int j = 0; j < VL; ++j) {
-                const int piece = lane * VL + j;          // 16 B pieces, DVS/8 per token
-                rv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    r_v, (piece / (DVS / 8)) * kv_row + (piece % (DVS / 8)) * 16, 0, 0));
+            for (int u = 0; u < 4; ++u) {
+                const int t = 4 * tg + u;
+                rg[u] = BufLoad<__bf16, CPT>::load(r_g, t * g_row + c0 * 2);
+                rk[u] = BufLoad<__bf16, CPT>::load(r_k, t * kv_row + c0 * 2);
+                rq[u] = BufLoad<__bf16, CPT>::load(r_q, t * kv_row + c0 * 2);
             }
             const rsrc_t r_b = make_rsrc(beta + t0 * H + head, (uint32_t)(valid * b_row));
-            rbl = BufLoad<__bf16, 1>::load(r_b, lr * b_row);
+            rbl = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, lr * b_row, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rb4[i] = BufLoad<__bf16, 1>::load(r_b, (4 * lq + i) * b_row);
+            for (int i = 0; i < 4; ++i)
+                rb4[i] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, (4 * lq + i) * b_row, 0, 0);
         };
         if (pw < n_chunks) issue_loads(pw);
+        PIPE_PROF_INIT();
 
         for (int64_t ci = pw; ci < n_chunks; ci += kNP) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
             if (!wait_at_least(&released[s], NC * round, stop)) break;
             char* slot = smem + s * SLOT;
+            char* kip = smem + Cfg::O_KI + pw * 16 * PK;
+            PIPE_PROF_MARK(0);
+            PIPE_PROF_VMWAIT(5);
 
-            // ---- decay products, lanes on channels, serial over tokens ------
-            float a[16][CPL], F[CPL];
+            // ---- decay products ---------------------------------------------
+            // a_t = e^{g_t}; F_t = e^{G_t} (product up to t), R_t = e^{G_15-G_t}
+            // (product after t); within the lane's 4 tokens, then across rows.
+            // Four channels at a time (one 8-byte piece of every tile).
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) F[j] = 1.f;
+            for (int h = 0; h < CPT / 4; ++h) {
+                float a[4][4], fl[4][4];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float gv[CPL], kv[CPL], qv[CPL], kt[CPL], qt[CPL];
-                RawVec<__bf16, CPL>::unpack(rg[t], gv);
-                RawVec<__bf16, CPL>::unpack(rk[t], kv);
-                RawVec<__bf16, CPL>::unpack(rq[t], qv);
+                for (int u = 0; u < 4; ++u) {
+                    float gv[CPT];
+                    RawVec<__bf16, CPT>::unpack(rg[u], gv);
 #pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    a[t][j] = fast_exp2(clamp_log_decay(gv[j]) * kLog2e);
-                    F[j] *= a[t][j];                      // e^{G_t}
-                    kt[j] = kv[j] * F[j];
-                    qt[j] = qv[j] * F[j];
+                    for (int j = 0; j < 4; ++j) {
+                        a[u][j] = fast_exp2(clamp_log_decay(gv[4 * h + j]) * kLog2e);
+                        fl[u][j] = u == 0 ? a[u][j] : fl[u - 1][j] * a[u][j];
+                    }
                 }
-                RawVec<__bf16, CPL>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KT + t * PK) + perm_pos(c0), kt);
-                RawVec<__bf16, CPL>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_QT + t * PK) + perm_pos(c0), qt);
-            }
-            float inv_end[CPL], R[CPL];
+                float pre[4], suf[4], fend[4], inv_end[4];
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                inv_end[j] = fast_rcp(F[j]);              // e^{-G_15} <= e^80
-                R[j] = 1.f;
-            }
-#pragma unroll
-            for (int t = 15; t >= 0; --t) {
-                float kv[CPL], kh[CPL], ki[CPL];
-                RawVec<__bf16, CPL>::unpack(rk[t], kv);
-#pragma unroll
-                for (int j = 0; j < CPL; ++j) {
-                    kh[j] = kv[j] * R[j];                 // R = e^{G_15 - G_t}
-                    ki[j] = kv[j] * (R[j] * inv_end[j]);  // e^{-G_t}
-                    R[j] *= a[t][j];
+                for (int j = 0; j < 4; ++j) {
+                    const float tot = fl[3][j];                 // this row's 4-token product
+                    const float nb = pair_row(tot, tg);         // row tg ^ 1
+                    const int pp = __builtin_bit_cast(int, tot * nb);   // rows 0-1 / rows 2-3 products
+                    const auto h32 = __builtin_amdgcn_permlane32_swap(pp, pp, false, false);
+                    const float lo = __builtin_bit_cast(float, (int)h32[0]);   // rows 0 and 1
+                    const float hi = __builtin_bit_cast(float, (int)h32[1]);   // rows 2 and 3
+                    pre[j] = (tg >= 2 ? lo : 1.f) * ((tg & 1) ? nb : 1.f);
+                    suf[j] = (tg <= 1 ? hi : 1.f) * ((tg & 1) ? 1.f : nb);
+                    fend[j] = lo * hi;                          // e^{G_15}
+                    inv_end[j] = fast_rcp(fend[j]);             // e^{-G_15} <= e^80
                 }
-                RawVec<__bf16, CPL>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KH + t * PH) + c0, kh);
-                RawVec<__bf16, CPL>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KI + t * PK) + perm_pos(c0), ki);
-            }
-            // e^{G_15} per channel, laid out for the consumers' row broadcasts:
-            // channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2]
+                const int pos = perm_pos(c0 + 4 * h);
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-                const int c = c0 + j;
-                const int kt = c >> 4, qq = (c >> 2) & 3, i = c & 3;
-                reinterpret_cast<float*>(slot + Cfg::O_GM)[(qq * 16 + 2 * kt + (i >> 1)) * 2 + (i & 1)] = F[j];
-            }
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 4 * tg + u;
+                    float kv[CPT], qv[CPT], kt[4], qt[4], kh[4], ki[4];
+                    RawVec<__bf16, CPT>::unpack(rk[u], kv);
+                    RawVec<__bf16, CPT>::unpack(rq[u], qv);
 #pragma unroll
-            for (int j = 0; j < VL; ++j) {
-                const int piece = lane * VL + j;
-                *reinterpret_cast<u32x4*>(slot + Cfg::O_V + (piece / (DVS / 8)) * PV + (piece % (DVS / 8)) * 16) = rv[j];
+                    for (int j = 0; j < 4; ++j) {
+                        const float rl = u == 3 ? 1.f : u == 2 ? a[3][j] : u == 1 ? a[3][j] * a[2][j]
+                                                                        : a[3][j] * a[2][j] * a[1][j];
+                        const float F = pre[j] * fl[u][j];
+                        const float R = suf[j] * rl;
+                        kt[j] = kv[4 * h + j] * F;
+                        qt[j] = qv[4 * h + j] * F;
+                        kh[j] = kv[4 * h + j] * R;
+                        // e^{-G_t} = R e^{-G_15}; a k so small that k R underflows
+                        // (|k| < 5e-6 at the steepest decay) contributes below
+                        // bf16 resolution either way
+                        ki[j] = kh[j] * inv_end[j];
+                    }
+                    // permuted tiles: the 4-channel piece lands at its position
+                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KT + t * PK) + pos, kt);
+                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_QT + t * PK) + pos, qt);
+                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(kip + t * PK) + pos, ki);
+                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KH + t * PH) + c0 + 4 * h, kh);
+                }
+                // e^{G_15} per channel, laid out for the consumers' row
+                // broadcasts: channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2];
+                // a group of 4 channels is one contiguous 16 B block
+                if (tg == 0) {
+                    const int c = c0 + 4 * h;
+                    const int kt = c >> 4, qq = (c >> 2) & 3;
+                    *reinterpret_cast<floatx4*>(slot + Cfg::O_GM + (qq * 16 + 2 * kt) * 8) =
+                        floatx4{fend[0], fend[1], fend[2], fend[3]};
+                }
             }
-            const float bl = (float)rbl;
+            const float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
             float b4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) b4[i] = (float)rb4[i];
+            for (int i = 0; i < 4; ++i) b4[i] = __builtin_bit_cast(float, rb4[i] << 16);
+            PIPE_PROF_MARK(1);
 
             // the next chunk of this wave streams in while this one finishes
             if (ci + kNP < n_chunks) issue_loads(ci + kNP);
+            PIPE_PROF_MARK(2);
 
             // ---- A_kk^T, A_qk^T (16x16x32 MFMA over the key channels) -------
             floatx4 akk = zero4(), aqk = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int off = lr * PK + (32 * ks + 8 * lq) * 2;
-                const bf16x8 fi = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_KI + off);
+                const bf16x8 fi = *reinterpret_cast<const bf16x8*>(kip + off);
                 const bf16x8 fk = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_KT + off);
                 const bf16x8 fq = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_QT + off);
                 akk = mfma32(fi, fk, akk);     // [s][r] = A_kk[r][s]
@@ -340,36 +449,41 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             *reinterpret_cast<shortx4*>(slot + Cfg::O_AQ + lane * 8) =
                 pack4(4 * lq + 0 <= lr ? aqk[0] : 0.f, 4 * lq + 1 <= lr ? aqk[1] : 0.f,
                       4 * lq + 2 <= lr ? aqk[2] : 0.f, 4 * lq + 3 <= lr ? aqk[3] : 0.f);
+            PIPE_PROF_MARK(3);
 
             // ---- Y = (I + N)^{-1}, N = (diag(beta) A_kk)^T strictly upper ----
-            // Column-oriented back substitution; lane (q, c) holds Y[4q+i][c].
-            float nv[4], y[4];
+            // -N[4q+i][r] = -beta_r A_kk[r][4q+i] sits in lane (q, r); spread
+            // every row of it to all four lane rows, then back-substitute.
+            float np[16], y[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                nv[i] = (4 * lq + i < lr) ? bl * akk[i] : 0.f;   // N[4q+i][r] = beta_r A_kk[r][4q+i]
-                y[i] = (4 * lq + i == lr) ? 1.f : 0.f;
+                float rows[4];
+                all_rows((4 * lq + i < lr) ? -bl * akk[i] : 0.f, rows);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) np[4 * g4 + i] = rows[g4];
             }
-#define KDA_BACK_STEP(m)                                                   \
-    {                                                                      \
-        const float ym = rows_from<((m) >> 2)>(y[(m) & 3]);                  \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                      \
-            y[i] = __builtin_fmaf(-row_bcast<(m)>(nv[i]), ym, y[i]);      \
-    }
-            KDA_BACK_STEP(15) KDA_BACK_STEP(14) KDA_BACK_STEP(13) KDA_BACK_STEP(12)
-            KDA_BACK_STEP(11) KDA_BACK_STEP(10) KDA_BACK_STEP(9) KDA_BACK_STEP(8)
-            KDA_BACK_STEP(7) KDA_BACK_STEP(6) KDA_BACK_STEP(5) KDA_BACK_STEP(4)
-            KDA_BACK_STEP(3) KDA_BACK_STEP(2) KDA_BACK_STEP(1)
-#undef KDA_BACK_STEP
-            // M'[r][4q+e] = X[r][4q+e] beta[4q+e], X = Y^T: lane (q, r) holds it in y[e]
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[r] = np[r];
+            back_subst(y, np);
+            // M'[r][4q+e] = X[r][4q+e] beta[4q+e], X = Y^T: lane (q, r) takes
+            // y[4q+e] plus the identity
+            float ye[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ye[e] = (lq == 0 ? y[e] : lq == 1 ? y[4 + e] : lq == 2 ? y[8 + e] : y[12 + e]) +
+                        (4 * lq + e == lr ? 1.f : 0.f);
             *reinterpret_cast<shortx4*>(slot + Cfg::O_MP + lane * 8) =
-                pack4(y[0] * b4[0], y[1] * b4[1], y[2] * b4[2], y[3] * b4[3]);
+                pack4(ye[0] * b4[0], ye[1] * b4[1], ye[2] * b4[2], ye[3] * b4[3]);
 
             flag_store(&ready[s], round + 1, lane);
+            PIPE_PROF_MARK(4);
         }
+        PIPE_PROF_FLUSH(0, pw == 0);
         return;
     }
 
     // ======================== consumer wave ==================================
+    if (KDA_PIPE_CONSUMER_PRIO > 0) __builtin_amdgcn_s_setprio(KDA_PIPE_CONSUMER_PRIO);
     const int w = wave;                      // value columns n0 + 16w .. +15
     floatx4 S[NKT];
     const int64_t sbase = ((int64_t)seq * H + head) * DK * DV + n0 + 16 * w + lr;
@@ -382,12 +496,34 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) S[kt] = zero4();
     }
+    // V tile of a chunk in accumulator layout -- lane (q, c) loads tokens
+    // 4q .. 4q+3 of column 16w + c -- two chunks ahead, as zero-extended
+    // 32-bit words (16-bit values would be packed in pairs, forcing a wait)
+    const int kv_row = (int)(stride * 2);
+    // (past the last chunk the resource covers no bytes and the loads return
+    // zeros: the registers are always written, so no copy has to wait for
+    // loads still in flight)
+    auto load_v = [&](int64_t ci, uint32_t (&vr)[4]) {
+        const int64_t t0 = t_begin + ci * 16;
+        const int64_t rem = t_end - t0;
+        const int valid = (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
+        const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0 + 16 * w,
+                                     (uint32_t)(valid * kv_row));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vr[e] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_v, (4 * lq + e) * kv_row + lr * 2, 0, 0);
+    };
+    uint32_t va[4] = {0, 0, 0, 0}, vb[4] = {0, 0, 0, 0};
+    load_v(0, va);
+    load_v(1, vb);
     bool ok = true;
-    for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    PIPE_PROF_INIT();
+    auto step = [&](int64_t ci, uint32_t (&vr)[4]) -> bool {
         const int s = (int)(ci % kRing);
         const int round = (int)(ci / kRing);
-        if (!wait_at_least(&ready[s], round + 1, stop)) { ok = false; break; }
+        if (!wait_at_least(&ready[s], round + 1, stop)) return false;
         const char* slot = smem + s * SLOT;
+        PIPE_PROF_MARK(0);
 
         bf16x8 fk[NKS], fq[NKS];
 #pragma unroll
@@ -397,18 +533,23 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             fq[ks] = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_QT + off);
         }
         const int tr_row = 4 * lq + (lr >> 2), tr_col = 4 * (lr & 3);
-        const bf16v4 vv = lds_read_tr(slot + Cfg::O_V + tr_row * PV + (16 * w + tr_col) * 2);
         bf16v4 kh[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) kh[kt] = lds_read_tr(slot + Cfg::O_KH + tr_row * PH + (16 * kt + tr_col) * 2);
         const shortx4 mp = *reinterpret_cast<const shortx4*>(slot + Cfg::O_MP + lane * 8);
         const shortx4 aq = *reinterpret_cast<const shortx4*>(slot + Cfg::O_AQ + lane * 8);
         const floatx2 gm = *reinterpret_cast<const floatx2*>(slot + Cfg::O_GM + (lq * 16 + lr) * 8);
+        // every operand of this chunk is in registers once these reads are
+        // done; the LDS performs a wave's operations in order, so the slot can
+        // be handed back before the arithmetic
+        flag_add(&released[s], 1, lane);
 
-        // Z' = Kt S - V  and  O = Qt S   (S as permuted bf16 B operands)
+        // Z' = Kt S - V  and  O^T = S^T Qt^T   (S as permuted bf16 operands:
+        // the same registers are the B operand of S and the A operand of S^T)
         floatx4 z, oa = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = -(float)vv[e];
+        for (int e = 0; e < 4; ++e) z[e] = -__builtin_bit_cast(float, vr[e] << 16);
+        load_v(ci + 2, vr);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             bf16x8 sb;
@@ -418,23 +559,41 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 sb[4 + e] = (__bf16)S[2 * ks + 1][e];
             }
             z = mfma32(fk[ks], sb, z);
-            oa = mfma32(fq[ks], sb, oa);
+            oa = mfma32(sb, fq[ks], oa);
         }
         // U = M' (V - Kt S): the accumulator layout is the 16x16x16 B layout
         const floatx4 u = mfma16(mp, pack4(-z[0], -z[1], -z[2], -z[3]), zero4());
         const shortx4 ub = pack4(u[0], u[1], u[2], u[3]);
-        oa = mfma16(aq, ub, oa);
+        // O^T += U^T A_qk^T: U's accumulator is the A operand of U^T, and the
+        // A_qk operand registers are the B operand of A_qk^T
+        oa = mfma16(ub, aq, oa);
         // S <- diag(e^{G_15}) S + Kh^T U
         state_update<0, NKT>(S, kh, ub, gm);
-        flag_add(&released[s], 1, lane);
+        PIPE_PROF_MARK(1);
 
+        // lane (q, t) holds O[t][16w + 4q .. +3]: one 8-byte store per lane;
+        // the resource covers the chunk's valid rows, so rows past the end of
+        // the sequence are dropped without a branch
         const int64_t tok0 = t_begin + ci * 16;
         const int valid = (int)((t_end - tok0) < 16 ? (t_end - tok0) : 16);
-        __bf16* op = o + (tok0 * H + head) * DV + n0 + 16 * w + lr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * lq + i < valid) op[(int64_t)(4 * lq + i) * H * DV] = (__bf16)oa[i];
+        const rsrc_t r_o = make_rsrc(o + (tok0 * H + head) * DV + n0 + 16 * w,
+                                     (uint32_t)(valid * H * DV * 2));
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, pack4(oa[0], oa[1], oa[2], oa[3])), r_o,
+            lr * H * DV * 2 + 8 * lq, 0, 0);
+        PIPE_PROF_MARK(2);
+        return true;
+    };
+    // whole pairs in the loop and an odd last chunk after it: every path
+    // through the loop body issues the same memory operations, which keeps
+    // the compiler's waits on the V loads exact
+    int64_t ci = 0;
+    for (; ci + 1 < n_chunks; ci += 2) {
+        if (!step(ci, va)) { ok = false; break; }
+        if (!step(ci + 1, vb)) { ok = false; break; }
     }
+    if (ok && ci < n_chunks && !step(ci, va)) ok = false;
+    PIPE_PROF_FLUSH_CONSUMER(w);
     if (sT != nullptr) {
         const float nan = __builtin_nanf("");
 #pragma unroll

@@ -52,6 +52,7 @@ __device__ __forceinline__ void store8(__bf16* p, const float v[8]) {
 
 // Non-temporal variants for data streamed once (no reuse through the caches).
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
     const floatx4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
     __builtin_nontemporal_store(a, reinterpret_cast<floatx4*>(p));
@@ -127,6 +128,7 @@ struct RawVec<float, 1> {
     static __device__ __forceinline__ void store(float* p, const float v[1]) { *p = v[0]; }
 };
 template <> struct RawVec<__bf16, 2> : RawVecImpl<2, bf16x2, __bf16> {};
+template <> struct RawVec<__bf16, 4> : RawVecImpl<4, bf16x4, __bf16> {};
 template <> struct RawVec<__bf16, 8> : RawVecImpl<8, bf16x8, __bf16> {};
 template <> struct RawVec<float, 2> : RawVecImpl<2, floatx2, float> {};
 template <> struct RawVec<float, 8> : RawVecImpl<8, floatx8, float> {};
@@ -154,6 +156,12 @@ template <>
 struct BufLoad<__bf16, 2> {
     static __device__ __forceinline__ bf16x2 load(rsrc_t r, int off) {
         return __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+};
+template <>
+struct BufLoad<__bf16, 4> {
+    static __device__ __forceinline__ bf16x4 load(rsrc_t r, int off) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
     }
 };
 template <>

@@ -142,7 +142,7 @@ CHUNK_CASES = [
     ("bf16", 64, 4, [190], False, 64, True, -0.05),
     ("bf16", 128, 2, [0, 5, 64, 130, 1, 0, 65], True, 64, True, -0.05),
     ("bf16", 128, 2, [100, 100, 100], False, 64, False, -5.0),
-    # 16-token chunks: producer / consumer kernel (ring of 6 LDS slots)
+    # 16-token chunks: producer / consumer kernel (ring of 8 LDS slots)
     ("bf16", 128, 4, [300], False, 16, True, -5.0),
     ("bf16", 128, 4, [300], False, 16, True, -0.05),
     ("bf16", 64, 4, [190], False, 16, True, -0.05),
