@@ -1,7 +1,7 @@
 """Benchmark of the KDA token mixer on one MI355X.
 
 A step is one pass of the prefill path over the long-context workload
-(B = 1, T = 65,536, 96 heads x 128, bf16 I/O, fp32 state, chunk 64):
+(B = 1, T = 65,536, 96 heads x 128, bf16 I/O, fp32 state, 16-token chunks):
 kda_conv -> kda_chunk_prefill -> kda_gated_norm, inputs resident in HBM.
 ``value`` is prefill tokens/s.  The decode step (B = 256, 64 consecutive
 steps) is timed in the same run and reported as TB/s under ``decode``.
@@ -28,7 +28,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_prefill_T65536_traffic.json")
 CHUNK_SOURCES = [os.path.join(ROOT, "linear_attention_recurrence_09_amd", "csrc", f)
-                 for f in ("kda_chunk.hip", "kda_device.hpp")]
+                 for f in ("kda_chunk_pipe.hip", "kda_chunk.hip", "kda_device.hpp")]
+CHUNK_KERNEL = "chunk_pipe_kernel<DK=128, 64 value columns> (kda_chunk_prefill, chunk 16)"
 
 
 def log(msg):
@@ -68,11 +69,19 @@ def prefill_bytes(N, H, D, n_seqs, es=2):
     return dict(conv=conv, chunk=chunk, norm=norm)
 
 
-def chunk_flops(N, H, D, C=64):
-    """Algorithmic FLOPs of the chunked recurrence (triangular-exact WY form)."""
-    per_token_head = 6 * D * D + (C * (C - 1) * D + 2 * C * (C + 1) * D + 2 * C * (C + 1) * D
-                                  + C ** 3 / 3) / C
-    return per_token_head * N * H
+def chunk_flops(N, H, D, C=16):
+    """Algorithmic FLOPs of the chunked recurrence, triangular-exact: per chunk
+    A_kk (strictly lower) and A_qk (lower) over D channels, the unit triangular
+    inverse (C^3/3), U = M'(V - K~S), O = Q~S + A_qk U and the state update."""
+    per_chunk = (C * (C - 1) * D          # A_kk
+                 + C * (C + 1) * D        # A_qk
+                 + C ** 3 / 3             # inverse
+                 + 2 * C * D * D          # K~ S
+                 + C * (C + 1) * D        # M' Z
+                 + 2 * C * D * D          # Q~ S
+                 + C * (C + 1) * D        # A_qk U
+                 + 2 * C * D * D)         # K^^T U
+    return per_chunk / C * N * H
 
 
 def decode_bytes(B, H, D, es=2):
@@ -143,7 +152,8 @@ def main():
     torch.cuda.set_device(0)
     kda.lib()
     spec = synth.CONFIGS[2]
-    H, D, C = spec.H, spec.D, spec.chunk
+    H, D = spec.H, spec.D
+    C = spec.chunk or 16        # 0 selects the library's fastest variant: 16 for bf16
     HD = H * D
     log(f"drawing inputs for {spec.name}")
     inp = synth.prefill_inputs(spec, device="cuda")
@@ -229,7 +239,7 @@ def main():
                    "T": N, "H": H, "D": D, "chunk": C, "sequences": 1, "state": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "chunk_kernel (kda_chunk_prefill)",
+                     "kernel": CHUNK_KERNEL,
                      "algorithmic_bytes_per_launch": nbytes["chunk"],
                      "avg_launch_ms": k_ms["chunk"],
                      "mfma_tflops_algorithmic": flops / (k_ms["chunk"] * 1e-3) / 1e12,

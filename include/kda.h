@@ -114,8 +114,9 @@ int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
  *                  initial_state (updated in place)
  *   chunk          tokens per chunk: 16, 32 or 64 (bf16; 16 is the fastest
  *                  and runs on separate producer and consumer waves); 16, 32
- *                  or 64 (fp32, where DK = 128 allows at most 32); the result
- *                  does not depend on it beyond rounding
+ *                  or 64 (fp32, where DK = 128 allows at most 32); 0 picks the
+ *                  fastest (16 for bf16; 32 for fp32 with DK = 128, else 64).
+ *                  The result does not depend on it beyond rounding
  * o must not overlap any input.  Unsupported (dtype, DK, DV, chunk)
  * combinations return KDA_ERR_UNSUPPORTED.
  */

@@ -110,7 +110,7 @@ def kda_conv(x, w, y, B, T, H, D, conv_state_in=None, conv_state_out=None, cu_se
                                       D, _dtype(x), l2_eps, _stream(stream)))
 
 
-def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, chunk=64,
+def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, chunk=0,
                       initial_state=None, final_state=None, cu_seqlens=None, num_seqs=0,
                       stream=None):
     """Chunkwise gated delta rule (see kda_chunk_prefill in kda.h).
@@ -153,7 +153,7 @@ def kda_gated_norm(o, gate, weight, y, n_tokens, H, D, eps=1e-6, stream=None):
 
 def kda_prefill(x, w, g, beta, gate, norm_w, H, D, cu_seqlens=None, num_seqs=1, B=1, T=None,
                 conv_state_in=None, conv_state_out=None, initial_state=None, final_state=None,
-                chunk=64, l2_eps=1e-6, rms_eps=1e-6, stream=None):
+                chunk=0, l2_eps=1e-6, rms_eps=1e-6, stream=None):
     """The whole prefill path as three C ABI calls on one stream:
     kda_conv -> kda_chunk_prefill (reading q, k, v in place from the conv
     output) -> kda_gated_norm.  Returns (y_qkv, o, y)."""

@@ -737,6 +737,7 @@ hipError_t launch_chunk_t(const void* q, const void* k, const void* v, int64_t s
 // exceeds the LDS budget).
 ChunkPlan plan_chunk(int dtype, int DK, int DV, int chunk, int64_t n_chains) {
     ChunkPlan p{0, 0, false, false};
+    if (chunk == 0) chunk = dtype == 1 ? 16 : (DK == 128 ? 32 : 64);   // fastest variant
     if (chunk != 16 && chunk != 32 && chunk != 64) return p;
     p.nb = chunk / 16;
     if (dtype == 1) {

@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 COPY_BYTES = 2 * 1024 ** 3
-CHUNK_TAG = "chunk_kernel"
+CHUNK_TAG = "chunk_pipe_kernel"
 COPY_TAG = "vectorized_elementwise_kernel"
 
 
@@ -77,8 +77,7 @@ def main():
     wb = statistics.mean(w_chunk) * 1024 * w_scale
     algo = bench.prefill_bytes(65536, 96, 128, 1)["chunk"]
     rec = {
-        "kernel": "chunk_kernel<bf16, DK=128, DV slice=64, chunk=64> (kda_chunk_prefill), "
-                  "T=65536, H=96",
+        "kernel": bench.CHUNK_KERNEL + ", T=65536, H=96",
         "source_sha256": bench.chunk_source_hash(),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters",

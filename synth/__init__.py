@@ -36,7 +36,7 @@ class PrefillSpec:
     len_lo: int = 0
     len_hi: int = 0
     varlen: bool = False            # pass cu_seqlens (packed) rather than B x T
-    chunk: int = 64
+    chunk: int = 0                  # tokens per chunk; 0 = the library's fastest
     x_std: float = 1.0
     conv_w_std: float = 0.25
     g_lo: float = -5.0
