@@ -10,32 +10,35 @@
 //
 // Chunk form (exact re-association of the token recurrence).  For a chunk of
 // 16 tokens with entering state S, G_r = sum_{u<=r} g_u per channel:
-//   Kt = K e^G,  Qt = Q e^G,  Kh = K e^{G_15 - G},  Ki = K e^{-G}
+//   Kt = K e^G,  Qt = Q e^G,  Ki = K e^{-G}
 //   A_kk = strict_lower(Kt Ki^T),  A_qk = lower(Qt Ki^T)
 //   M' = (I + diag(beta) A_kk)^{-1} diag(beta)
 //   U  = M' (V - Kt S)
 //   O  = Qt S + A_qk U
-//   S <- diag(e^{G_15}) S + Kh^T U
+//   S <- diag(e^{G_15}) (S + Ki^T U)
 // A 16-token chunk spans at most e^{-80} of decay (g >= -5), so every factor
 // above is a finite fp32 / bf16 number and no intra-chunk splitting is needed.
 //
 // Work split.  One workgroup per (sequence, head, slice of 64 value columns).
-//  * Producer waves (4) build everything that does not depend on the state,
-//    one whole chunk per wave: per-channel decay products with lanes on
-//    channels (serial over the 16 tokens), the operand tiles Kt, Qt, Ki, Kh
-//    and V in LDS, A_kk^T and A_qk^T on MFMA, and the 16 x 16 unit triangular
-//    inverse by back substitution in registers (row broadcasts by DPP and the
-//    gfx950 cross-row lane swaps).  Results go to a ring of LDS slots.
+//  * Producer waves (8, two per SIMD) build everything that does not depend
+//    on the state, one whole chunk per wave: per-channel decay products with
+//    each lane holding all 16 tokens of its channels, the operand tiles -Kt,
+//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA, and the 16 x 16
+//    unit triangular inverse by back substitution in registers (row
+//    broadcasts by DPP and the gfx950 cross-row lane swaps).  Results go to a
+//    ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
-//    chunk (V - Kt S, Qt S, M' Z, A_qk U, decay, Kh^T U) is wave-local, so
+//    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
 //    consumers never wait on each other.  S feeds the next chunk's products as
 //    an in-register bf16 B operand: the contraction index is permuted to the
-//    accumulator's row order, and Kt / Qt are stored in LDS in that order.
+//    accumulator's row order, and -Kt / Qt are stored in LDS in that order.
+//    A consumer reads the next chunk's leading operands while it updates the
+//    state, and issues no global loads (V comes through the slot).
 //  * Slots are handed over through LDS counters (producer: "chunk ready",
-//    consumers: "slot released"), so producers run ahead of the consumers by
-//    up to the ring depth.  Every wait is bounded; a wait that runs out stops
-//    the workgroup and its final state is written as NaN.
+//    each consumer: "slot released"), so producers run ahead of the consumers
+//    by up to the ring depth.  Every wait is bounded; a wait that runs out
+//    stops the workgroup and its final state is written as NaN.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -83,6 +86,7 @@ namespace kda {
 namespace {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16v4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
 
@@ -108,18 +112,17 @@ struct PipeCfg {
     // read get 32 B (8 banks apart).
     static constexpr int PK = DK * 2 + 16;
     static constexpr int PH = DK * 2 + 32;
+    static constexpr int PV = DVS * 2 + 32;
     // one ring slot (a chunk handed to the consumers)
-    static constexpr int O_KT = 0;                      // K e^G       (permuted channels)
-    static constexpr int O_QT = O_KT + 16 * PK;         // Q e^G       (permuted channels)
-    static constexpr int O_KH = O_QT + 16 * PK;         // K e^{G15-G} (natural order)
-    static constexpr int O_MP = O_KH + 16 * PH;         // M' as 16x16x16 A operands
+    static constexpr int O_KT = 0;                      // K e^G   (permuted channels)
+    static constexpr int O_QT = O_KT + 16 * PK;         // Q e^G   (permuted channels)
+    static constexpr int O_KI = O_QT + 16 * PK;         // K e^{-G} (natural order)
+    static constexpr int O_V = O_KI + 16 * PH;          // V, this workgroup's columns
+    static constexpr int O_MP = O_V + 16 * PV;          // M' as 16x16x16 A operands
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    // K e^-G (permuted channels): read only by the producer that wrote it, so
-    // each producer wave has one private tile after the ring
-    static constexpr int O_KI = kRing * SLOT;
-    static constexpr int BYTES = O_KI + kNP * 16 * PK;
+    static constexpr int BYTES = kRing * SLOT;
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
@@ -144,9 +147,10 @@ __device__ __forceinline__ floatx4 mfma16(shortx4 a, shortx4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ shortx4 pack4(float a, float b, float c, float d) {
-    bf16x4 v;
-    v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
-    return __builtin_bit_cast(shortx4, v);
+    // two paired conversions (one v_cvt_pk_bf16_f32 each)
+    const bf16x2 lo = __builtin_convertvector(floatx2{a, b}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector(floatx2{c, d}, bf16x2);
+    return __builtin_bit_cast(shortx4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
 }
 
 // Transposed 8-byte LDS read (gfx950): lane j of each 16-lane group supplies
@@ -174,13 +178,6 @@ __device__ __forceinline__ void all_rows(float x, float (&out)[4]) {
     out[2] = __builtin_bit_cast(float, (int)e[1]);
     out[3] = __builtin_bit_cast(float, (int)o[1]);
 }
-// The value of the neighbouring row (row r ^ 1).
-__device__ __forceinline__ float pair_row(float x, int row) {
-    const int xi = __builtin_bit_cast(int, x);
-    const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);   // rows 0022 / 1133
-    return __builtin_bit_cast(float, (row & 1) ? (int)p16[0] : (int)p16[1]);
-}
-
 // y += (lane M of the row's n) * m, one v_fmac_f32 with a DPP row broadcast
 // on its first source.  The broadcast operand must not be written by a VALU
 // instruction in the two instructions before (see back_subst).
@@ -215,40 +212,66 @@ __device__ __forceinline__ void back_subst(float (&y)[16], const float (&np)[16]
     back_subst_steps<15>(y, np);
 }
 
-// S[KT..] <- diag(e^{G_15}) S + Kh^T U for the key tiles KT .. NKT-1.  Row i
-// of tile KT is channel 16 KT + 4q + i; its decay sits in lane 2 KT + i/2 of
-// the lane's own row, component i % 2.
+// Rows of the state tiles KT .. NKT-1 times their decay e^{G_15}: row i of
+// tile KT is channel 16 KT + 4q + i; its decay sits in lane 2 KT + i/2 of the
+// lane's own 16-lane row, component i % 2.
 template <int KT, int NKT>
-__device__ __forceinline__ void state_update(floatx4 (&S)[NKT], const bf16v4 (&kh)[NKT],
-                                             shortx4 ub, floatx2 gm) {
+__device__ __forceinline__ void decay_rows(floatx4 (&S)[NKT], floatx2 gm) {
     if constexpr (KT < NKT) {
         S[KT][0] *= row_bcast<2 * KT>(gm[0]);
         S[KT][1] *= row_bcast<2 * KT>(gm[1]);
         S[KT][2] *= row_bcast<2 * KT + 1>(gm[0]);
         S[KT][3] *= row_bcast<2 * KT + 1>(gm[1]);
-        S[KT] = mfma16(__builtin_bit_cast(shortx4, kh[KT]), ub, S[KT]);
-        state_update<KT + 1, NKT>(S, kh, ub, gm);
+        decay_rows<KT + 1, NKT>(S, gm);
     }
 }
 
 // ---- slot hand-over ----------------------------------------------------------
+// (every lane reads the same counter: the value is made wave-uniform, so the
+// polling loops branch on scalars)
 __device__ __forceinline__ int flag_load(int* f) {
-    return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 // Counter updates are made by lane 0 only: an atomic executed by a whole
 // wave acts once per active lane.
 __device__ __forceinline__ void flag_store(int* f, int v, int lane) {
     if (lane == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void flag_add(int* f, int v, int lane) {
-    if (lane == 0) __hip_atomic_fetch_add(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Wait until all N counters f[0..N-1] are >= target (N = 4: one 16-byte
+// read).  Returns false (and raises the workgroup's stop flag) if the wait runs
+// out, or if another wave has raised it.
+template <int N>
+__device__ __forceinline__ bool wait_all_at_least(int* f, int target, int* stop) {
+    static_assert(N == 4, "one 16-byte read of the consumer counters");
+    int n = 0;
+    for (;;) {
+        const intx4 v = *reinterpret_cast<const volatile intx4*>(f);
+        const int m = __builtin_amdgcn_readfirstlane(min(min(v[0], v[1]), min(v[2], v[3])));
+        if (m >= target) break;
+        if (__builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
+            return false;
+        if (++n > kSpinLimit) {
+            __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(KDA_PIPE_SLEEP);
+    }
+    // the slot is written only after the counters were seen (the LDS serves
+    // a wave's operations in order; the compiler keeps the writes below)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return true;
 }
+
 // Wait until *f >= target.  Returns false (and raises the workgroup's stop
 // flag) if the wait runs out, or if another wave has raised it.
 __device__ __forceinline__ bool wait_at_least(int* f, int target, int* stop) {
     int n = 0;
     while (flag_load(f) < target) {
-        if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) return false;
+        if (__builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
+            return false;
         if (++n > kSpinLimit) {
             __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
@@ -270,10 +293,12 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
-    __shared__ int flags[2 * kRing + 1];   // ready[kRing], released[kRing], stop
+    // ready[kRing], released[kRing][NC] (one counter per consumer), stop
+    constexpr int NFLAGS = kRing + kRing * NC + 1;
+    __shared__ __attribute__((aligned(16))) int flags[NFLAGS];
     int* ready = flags;
     int* released = flags + kRing;
-    int* stop = flags + 2 * kRing;
+    int* stop = flags + kRing + kRing * NC;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -305,133 +330,139 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int64_t t_end = cu ? (int64_t)cu[seq + 1] : t_begin + T_len;
     const int64_t n_chunks = (t_end - t_begin + 15) / 16;
 
-    if (tid < 2 * kRing + 1) flags[tid] = 0;
+    if (tid < NFLAGS) flags[tid] = 0;
     __syncthreads();
 
     if (wave >= NC) {
         // ===================== producer wave =================================
-        // Stage-1 lane layout: lane (row tg, column cg) holds channels
-        // cg*CPT .. cg*CPT+CPT-1 of tokens 4tg .. 4tg+3 -- one wide load per
-        // token and tensor.  Decay products run serially over the lane's four
-        // tokens; the products over the other rows come from cross-row swaps.
+        // Stage-1 lane layout: lane l holds channels CPL*l .. CPL*l+CPL-1 of
+        // all 16 tokens (one 4- or 2-byte load per token and tensor), so the
+        // decay products over the chunk run serially inside the lane.
         const int pw = wave - NC;
-        constexpr int CPT = Cfg::CPT;
-        const int tg = lane >> 4, cg = lane & 15;
-        const int c0 = cg * CPT;
-        using RawT = typename RawVec<__bf16, CPT>::type;
-        RawT rg[4], rk[4], rq[4];
+        constexpr int CPL = DK / 64;
+        const int c0 = CPL * lane;
+        uint32_t rg[16], rk[16], rq[16];   // CPL bf16 channels per word
+        // V slice of the chunk: lane holds token lane/4, columns 16 (lane%4) .. +15
+        bf16x8 rv[2];
         // beta as zero-extended 32-bit words: 16-bit values would be packed in
         // pairs right after the loads, which makes the wave wait for them
         uint32_t rbl, rb4[4];
         const int g_row = H * DK * 2, kv_row = (int)(stride * 2), b_row = H * 2;
+        const int vt = lane >> 2, vc = 16 * (lane & 3);
+        auto load_word = [](rsrc_t r, int off) -> uint32_t {
+            if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+            else return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        };
+        // Loads of chunk ci.  Past the last chunk the resources cover no bytes
+        // and the loads return zeros; they are issued anyway, so that every
+        // iteration issues the same memory operations and no register copy
+        // has to wait for loads still in flight.
         auto issue_loads = [&](int64_t ci) {
             const int64_t t0 = t_begin + ci * 16;
             const int64_t rem = t_end - t0;
-            const int valid = (int)(rem < 16 ? rem : 16);
+            const int valid = (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
             const rsrc_t r_g = make_rsrc(g + (t0 * H + head) * DK, (uint32_t)(valid * g_row));
             const rsrc_t r_k = make_rsrc(k + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
             const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
+            const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = 4 * tg + u;
-                rg[u] = BufLoad<__bf16, CPT>::load(r_g, t * g_row + c0 * 2);
-                rk[u] = BufLoad<__bf16, CPT>::load(r_k, t * kv_row + c0 * 2);
-                rq[u] = BufLoad<__bf16, CPT>::load(r_q, t * kv_row + c0 * 2);
+            for (int t = 0; t < 16; ++t) {
+                rg[t] = load_word(r_g, t * g_row + c0 * 2);
+                rk[t] = load_word(r_k, t * kv_row + c0 * 2);
+                rq[t] = load_word(r_q, t * kv_row + c0 * 2);
             }
+            rv[0] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2);
+            rv[1] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2 + 16);
             const rsrc_t r_b = make_rsrc(beta + t0 * H + head, (uint32_t)(valid * b_row));
             rbl = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, lr * b_row, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 rb4[i] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, (4 * lq + i) * b_row, 0, 0);
         };
-        if (pw < n_chunks) issue_loads(pw);
+        // channel j of a word as fp32 (bf16 is the top half of an fp32)
+        auto chan = [](uint32_t w, int j) -> float {
+            return __builtin_bit_cast(float, j == 0 ? w << 16 : w & 0xffff0000u);
+        };
+        // CPL bf16 values as one word / half-word LDS store
+        auto put = [](char* p, const float (&x)[CPL]) {
+            if constexpr (CPL == 2) {
+                *reinterpret_cast<bf16x2*>(p) = bf16x2{(__bf16)x[0], (__bf16)x[1]};
+            } else {
+                *reinterpret_cast<__bf16*>(p) = (__bf16)x[0];
+            }
+        };
+        issue_loads(pw);
         PIPE_PROF_INIT();
 
-        for (int64_t ci = pw; ci < n_chunks; ci += kNP) {
+        // The loop has no early exit: an exit path would merge with the
+        // prefetch registers at the loop's latch and make every iteration wait
+        // for its loads.  A wait that runs out (the stop flag is then raised)
+        // lets the body run once more on whatever the slot holds, publishes
+        // nothing, and ends the loop.
+        const int pos = perm_pos(c0);   // this lane's channels in the permuted tiles
+        for (int64_t ci = pw; ci < n_chunks;) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
-            if (!wait_at_least(&released[s], NC * round, stop)) break;
+            const bool go = wait_all_at_least<NC>(&released[s * NC], round, stop);
             char* slot = smem + s * SLOT;
-            char* kip = smem + Cfg::O_KI + pw * 16 * PK;
             PIPE_PROF_MARK(0);
             PIPE_PROF_VMWAIT(5);
 
             // ---- decay products ---------------------------------------------
-            // a_t = e^{g_t}; F_t = e^{G_t} (product up to t), R_t = e^{G_15-G_t}
-            // (product after t); within the lane's 4 tokens, then across rows.
-            // Four channels at a time (one 8-byte piece of every tile).
+            // a_t = e^{g_t}; F_t = e^{G_t} = a_0 .. a_t (forward), then
+            // E_t = e^{-G_t} = e^{-G_15} a_{t+1} .. a_15 (backward)
+            float a[CPL][16], F[CPL];
 #pragma unroll
-            for (int h = 0; h < CPT / 4; ++h) {
-                float a[4][4], fl[4][4];
+            for (int t = 0; t < 16; ++t) {
+                float kt[CPL], qt[CPL];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float gv[CPT];
-                    RawVec<__bf16, CPT>::unpack(rg[u], gv);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        a[u][j] = fast_exp2(clamp_log_decay(gv[4 * h + j]) * kLog2e);
-                        fl[u][j] = u == 0 ? a[u][j] : fl[u - 1][j] * a[u][j];
-                    }
+                for (int j = 0; j < CPL; ++j) {
+                    a[j][t] = fast_exp2(clamp_log_decay(chan(rg[t], j)) * kLog2e);
+                    F[j] = t == 0 ? a[j][0] : F[j] * a[j][t];
+                    kt[j] = -(chan(rk[t], j) * F[j]);   // stored negated: -K e^G
+                    qt[j] = chan(rq[t], j) * F[j];
                 }
-                float pre[4], suf[4], fend[4], inv_end[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float tot = fl[3][j];                 // this row's 4-token product
-                    const float nb = pair_row(tot, tg);         // row tg ^ 1
-                    const int pp = __builtin_bit_cast(int, tot * nb);   // rows 0-1 / rows 2-3 products
-                    const auto h32 = __builtin_amdgcn_permlane32_swap(pp, pp, false, false);
-                    const float lo = __builtin_bit_cast(float, (int)h32[0]);   // rows 0 and 1
-                    const float hi = __builtin_bit_cast(float, (int)h32[1]);   // rows 2 and 3
-                    pre[j] = (tg >= 2 ? lo : 1.f) * ((tg & 1) ? nb : 1.f);
-                    suf[j] = (tg <= 1 ? hi : 1.f) * ((tg & 1) ? 1.f : nb);
-                    fend[j] = lo * hi;                          // e^{G_15}
-                    inv_end[j] = fast_rcp(fend[j]);             // e^{-G_15} <= e^80
-                }
-                const int pos = perm_pos(c0 + 4 * h);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int t = 4 * tg + u;
-                    float kv[CPT], qv[CPT], kt[4], qt[4], kh[4], ki[4];
-                    RawVec<__bf16, CPT>::unpack(rk[u], kv);
-                    RawVec<__bf16, CPT>::unpack(rq[u], qv);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float rl = u == 3 ? 1.f : u == 2 ? a[3][j] : u == 1 ? a[3][j] * a[2][j]
-                                                                        : a[3][j] * a[2][j] * a[1][j];
-                        const float F = pre[j] * fl[u][j];
-                        const float R = suf[j] * rl;
-                        kt[j] = kv[4 * h + j] * F;
-                        qt[j] = qv[4 * h + j] * F;
-                        kh[j] = kv[4 * h + j] * R;
-                        // e^{-G_t} = R e^{-G_15}; a k so small that k R underflows
-                        // (|k| < 5e-6 at the steepest decay) contributes below
-                        // bf16 resolution either way
-                        ki[j] = kh[j] * inv_end[j];
-                    }
-                    // permuted tiles: the 4-channel piece lands at its position
-                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KT + t * PK) + pos, kt);
-                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_QT + t * PK) + pos, qt);
-                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(kip + t * PK) + pos, ki);
-                    RawVec<__bf16, 4>::store(reinterpret_cast<__bf16*>(slot + Cfg::O_KH + t * PH) + c0 + 4 * h, kh);
-                }
-                // e^{G_15} per channel, laid out for the consumers' row
-                // broadcasts: channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2];
-                // a group of 4 channels is one contiguous 16 B block
-                if (tg == 0) {
-                    const int c = c0 + 4 * h;
-                    const int kt = c >> 4, qq = (c >> 2) & 3;
-                    *reinterpret_cast<floatx4*>(slot + Cfg::O_GM + (qq * 16 + 2 * kt) * 8) =
-                        floatx4{fend[0], fend[1], fend[2], fend[3]};
-                }
+                put(slot + Cfg::O_KT + t * PK + pos * 2, kt);
+                put(slot + Cfg::O_QT + t * PK + pos * 2, qt);
             }
-            const float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
+            float E[CPL];
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) E[j] = fast_rcp(F[j]);   // e^{-G_15} <= e^80
+#pragma unroll
+            for (int t = 15; t >= 0; --t) {
+                float ki[CPL];
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    if (t < 15) E[j] *= a[j][t + 1];
+                    ki[j] = chan(rk[t], j) * E[j];
+                }
+                put(slot + Cfg::O_KI + t * PH + c0 * 2, ki);
+            }
+            // e^{G_15} per channel, laid out for the consumers' row
+            // broadcasts: channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2]
+            {
+                const int kt = c0 >> 4, qq = (c0 >> 2) & 3, i = c0 & 3;
+                float* gp = reinterpret_cast<float*>(slot + Cfg::O_GM) + ((qq * 16 + 2 * kt + (i >> 1)) * 2 + (i & 1));
+                if constexpr (CPL == 2) *reinterpret_cast<floatx2*>(gp) = floatx2{F[0], F[1]};
+                else *gp = F[0];
+            }
+            *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
+            *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
+            // beta to fp32 before the next chunk's loads reuse its registers
+            // (a conversion sunk below them would keep both copies live and
+            // add a register move that waits for the loads)
+            float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
+            asm volatile("" : "+v"(bl));
             float b4[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) b4[i] = __builtin_bit_cast(float, rb4[i] << 16);
+            for (int i = 0; i < 4; ++i) {
+                b4[i] = __builtin_bit_cast(float, rb4[i] << 16);
+                asm volatile("" : "+v"(b4[i]));
+            }
             PIPE_PROF_MARK(1);
 
             // the next chunk of this wave streams in while this one finishes
-            if (ci + kNP < n_chunks) issue_loads(ci + kNP);
+            issue_loads(ci + kNP);
             PIPE_PROF_MARK(2);
 
             // ---- A_kk^T, A_qk^T (16x16x32 MFMA over the key channels) -------
@@ -439,10 +470,15 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const int off = lr * PK + (32 * ks + 8 * lq) * 2;
-                const bf16x8 fi = *reinterpret_cast<const bf16x8*>(kip + off);
+                // Ki is in natural channel order: the channels of permuted
+                // positions 8q .. 8q+7 are 4q .. 4q+3 and 16+4q .. 16+4q+3
+                const char* kir = slot + Cfg::O_KI + lr * PH + (32 * ks + 4 * lq) * 2;
+                const bf16x4 i0 = *reinterpret_cast<const bf16x4*>(kir);
+                const bf16x4 i1 = *reinterpret_cast<const bf16x4*>(kir + 32);
+                const bf16x8 fi = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
                 const bf16x8 fk = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_KT + off);
                 const bf16x8 fq = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_QT + off);
-                akk = mfma32(fi, fk, akk);     // [s][r] = A_kk[r][s]
+                akk = mfma32(fi, fk, akk);     // [s][r] = -A_kk[r][s] (the tile holds -Kt)
                 aqk = mfma32(fi, fq, aqk);     // [s][r] = A_qk[r][s]
             }
             // lane (q, r) holds A[r][4q+i]: exactly the 16x16x16 A operand of row r
@@ -458,7 +494,7 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float rows[4];
-                all_rows((4 * lq + i < lr) ? -bl * akk[i] : 0.f, rows);
+                all_rows((4 * lq + i < lr) ? bl * akk[i] : 0.f, rows);
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) np[4 * g4 + i] = rows[g4];
             }
@@ -475,8 +511,9 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             *reinterpret_cast<shortx4*>(slot + Cfg::O_MP + lane * 8) =
                 pack4(ye[0] * b4[0], ye[1] * b4[1], ye[2] * b4[2], ye[3] * b4[3]);
 
-            flag_store(&ready[s], round + 1, lane);
+            flag_store(&ready[s], round + 1, go ? lane : 1);
             PIPE_PROF_MARK(4);
+            ci = go ? ci + kNP : n_chunks;
         }
         PIPE_PROF_FLUSH(0, pw == 0);
         return;
@@ -496,103 +533,115 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) S[kt] = zero4();
     }
-    // V tile of a chunk in accumulator layout -- lane (q, c) loads tokens
-    // 4q .. 4q+3 of column 16w + c -- two chunks ahead, as zero-extended
-    // 32-bit words (16-bit values would be packed in pairs, forcing a wait)
-    const int kv_row = (int)(stride * 2);
-    // (past the last chunk the resource covers no bytes and the loads return
-    // zeros: the registers are always written, so no copy has to wait for
-    // loads still in flight)
-    auto load_v = [&](int64_t ci, uint32_t (&vr)[4]) {
-        const int64_t t0 = t_begin + ci * 16;
-        const int64_t rem = t_end - t0;
-        const int valid = (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
-        const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0 + 16 * w,
-                                     (uint32_t)(valid * kv_row));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            vr[e] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_v, (4 * lq + e) * kv_row + lr * 2, 0, 0);
-    };
-    uint32_t va[4] = {0, 0, 0, 0}, vb[4] = {0, 0, 0, 0};
-    load_v(0, va);
-    load_v(1, vb);
-    bool ok = true;
-    PIPE_PROF_INIT();
-    auto step = [&](int64_t ci, uint32_t (&vr)[4]) -> bool {
-        const int s = (int)(ci % kRing);
-        const int round = (int)(ci / kRing);
-        if (!wait_at_least(&ready[s], round + 1, stop)) return false;
-        const char* slot = smem + s * SLOT;
-        PIPE_PROF_MARK(0);
-
-        bf16x8 fk[NKS], fq[NKS];
+    // Software pipeline over the chunks.  The operands of a chunk's products
+    // with S (Kt, Qt) and V, M' are read while the previous chunk updates the
+    // state; Ki, A_qk and the decays at the start of the chunk, behind the
+    // Kt S products.  The loop has no early exit (an exit path would merge
+    // with the carried operand registers at the loop's latch and add a wait
+    // for them): a wait that runs out raises the stop flag and ends the loop
+    // through its condition.
+    const int tr_row = 4 * lq + (lr >> 2), tr_col = 4 * (lr & 3);
+    bf16x8 fk[NKS], fq[NKS];
+    bf16v4 vv;
+    shortx4 mp;
+    auto read_head = [&](const char* slot) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int off = lr * PK + (32 * ks + 8 * lq) * 2;
             fk[ks] = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_KT + off);
             fq[ks] = *reinterpret_cast<const bf16x8*>(slot + Cfg::O_QT + off);
         }
-        const int tr_row = 4 * lq + (lr >> 2), tr_col = 4 * (lr & 3);
-        bf16v4 kh[NKT];
+        // V in accumulator layout: tokens 4q .. 4q+3 of column 16w + c
+        // (transposed read: lane (q, c) receives rows 4q .. 4q+3 of column c)
+        vv = lds_read_tr(slot + Cfg::O_V + tr_row * Cfg::PV + (16 * w + tr_col) * 2);
+        mp = *reinterpret_cast<const shortx4*>(slot + Cfg::O_MP + lane * 8);
+    };
+    // the 16x16x16 identity as an A operand (lane (q, r): row r, k = 4q+e)
+    shortx4 ident;
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) kh[kt] = lds_read_tr(slot + Cfg::O_KH + tr_row * PH + (16 * kt + tr_col) * 2);
-        const shortx4 mp = *reinterpret_cast<const shortx4*>(slot + Cfg::O_MP + lane * 8);
+    for (int e = 0; e < 4; ++e) ident[e] = lr == 4 * lq + e ? (short)0x3F80 : (short)0;
+    const int nch = (int)n_chunks;
+    bool ok = nch == 0 || wait_at_least(&ready[0], 1, stop);
+    // the slot is read only after its counter was seen (the compiler keeps
+    // the reads below this point; the LDS serves a wave's operations in order)
+    asm volatile("" ::"s"((int)ok) : "memory");
+    read_head(smem);
+    // output: a pointer that advances one chunk of rows per step and the
+    // rows left in the sequence
+    const int o_row = H * DV * 2;   // bytes between tokens
+    const __bf16* o_chunk = o + (t_begin * H + head) * DV + n0 + 16 * w;
+    int rows_left = (int)(t_end - t_begin);
+    PIPE_PROF_INIT();
+    for (unsigned ci = ok ? 0u : (unsigned)nch; ci < (unsigned)nch;) {
+        const char* slot = smem + (ci % kRing) * SLOT;
+        // the rest of this chunk's operands
+        bf16v4 ki[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) ki[kt] = lds_read_tr(slot + Cfg::O_KI + tr_row * PH + (16 * kt + tr_col) * 2);
         const shortx4 aq = *reinterpret_cast<const shortx4*>(slot + Cfg::O_AQ + lane * 8);
         const floatx2 gm = *reinterpret_cast<const floatx2*>(slot + Cfg::O_GM + (lq * 16 + lr) * 8);
-        // every operand of this chunk is in registers once these reads are
-        // done; the LDS performs a wave's operations in order, so the slot can
-        // be handed back before the arithmetic
-        flag_add(&released[s], 1, lane);
+        // the next chunk's counter, read early (a value already at the target
+        // saves the polling round trip later)
+        const unsigned cn = ci + 1;
+        int* rdy = &ready[cn % kRing];
+        const int target = cn < (unsigned)nch ? (int)(cn / kRing) + 1 : 0;
+        const int peek = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        PIPE_PROF_MARK(0);
 
-        // Z' = Kt S - V  and  O^T = S^T Qt^T   (S as permuted bf16 operands:
-        // the same registers are the B operand of S and the A operand of S^T)
-        floatx4 z, oa = zero4();
+        // S as permuted bf16 operands: the same registers are the B operand of
+        // S and the A operand of S^T
+        bf16x8 sb[NKS];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = -__builtin_bit_cast(float, vr[e] << 16);
-        load_v(ci + 2, vr);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            bf16x8 sb;
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sb[e] = (__bf16)S[2 * ks][e];
-                sb[4 + e] = (__bf16)S[2 * ks + 1][e];
+                sb[ks][e] = (__bf16)S[2 * ks][e];
+                sb[ks][4 + e] = (__bf16)S[2 * ks + 1][e];
             }
-            z = mfma32(fk[ks], sb, z);
-            oa = mfma32(sb, fq[ks], oa);
-        }
+        // R = V - Kt S (the state chain) first, then O^T = S^T Qt^T, which
+        // fills the wait for R.  V enters through an identity product (its
+        // transposed read is the 16x16x16 B layout) and the Kt tile holds -Kt.
+        floatx4 z = mfma16(ident, __builtin_bit_cast(shortx4, vv), zero4());
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) z = mfma32(fk[ks], sb[ks], z);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 oa = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) oa = mfma32(sb[ks], fq[ks], oa);
+        __builtin_amdgcn_sched_barrier(0);
         // U = M' (V - Kt S): the accumulator layout is the 16x16x16 B layout
-        const floatx4 u = mfma16(mp, pack4(-z[0], -z[1], -z[2], -z[3]), zero4());
+        const floatx4 u = mfma16(mp, pack4(z[0], z[1], z[2], z[3]), zero4());
         const shortx4 ub = pack4(u[0], u[1], u[2], u[3]);
+        // S + Ki^T U, tile by tile (the decay follows below)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) S[kt] = mfma16(__builtin_bit_cast(shortx4, ki[kt]), ub, S[kt]);
         // O^T += U^T A_qk^T: U's accumulator is the A operand of U^T, and the
         // A_qk operand registers are the B operand of A_qk^T
         oa = mfma16(ub, aq, oa);
-        // S <- diag(e^{G_15}) S + Kh^T U
-        state_update<0, NKT>(S, kh, ub, gm);
+        // every read of this slot has been issued; the release waits for them
+        flag_store(&released[(ci % kRing) * NC + w], (int)(ci / kRing) + 1, lane);
+        // the next chunk's leading operands, read while the state updates
+        ok = __builtin_amdgcn_readfirstlane(peek) >= target || wait_at_least(rdy, target, stop);
+        asm volatile("" ::"s"((int)ok) : "memory");
+        read_head(smem + (cn % kRing) * SLOT);
+        // S <- diag(e^{G_15}) (S + Ki^T U): row i of tile kt is channel
+        // 16 kt + 4q + i; its decay sits in lane 2 kt + i/2 of the lane's own
+        // row, component i % 2
+        decay_rows<0, NKT>(S, gm);
         PIPE_PROF_MARK(1);
 
         // lane (q, t) holds O[t][16w + 4q .. +3]: one 8-byte store per lane;
-        // the resource covers the chunk's valid rows, so rows past the end of
-        // the sequence are dropped without a branch
-        const int64_t tok0 = t_begin + ci * 16;
-        const int valid = (int)((t_end - tok0) < 16 ? (t_end - tok0) : 16);
-        const rsrc_t r_o = make_rsrc(o + (tok0 * H + head) * DV + n0 + 16 * w,
-                                     (uint32_t)(valid * H * DV * 2));
+        // the resource covers the chunk's rows inside the sequence, so rows
+        // past its end are dropped without a branch
+        const rsrc_t r_o = make_rsrc(o_chunk, (uint32_t)((rows_left < 16 ? rows_left : 16) * o_row));
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(u32x2, pack4(oa[0], oa[1], oa[2], oa[3])), r_o,
-            lr * H * DV * 2 + 8 * lq, 0, 0);
+            lr * o_row + 8 * lq, 0, 0);
+        o_chunk += 16 * H * DV;
+        rows_left -= 16;
         PIPE_PROF_MARK(2);
-        return true;
-    };
-    // whole pairs in the loop and an odd last chunk after it: every path
-    // through the loop body issues the same memory operations, which keeps
-    // the compiler's waits on the V loads exact
-    int64_t ci = 0;
-    for (; ci + 1 < n_chunks; ci += 2) {
-        if (!step(ci, va)) { ok = false; break; }
-        if (!step(ci + 1, vb)) { ok = false; break; }
+        ci = ok ? cn : (unsigned)nch;
     }
-    if (ok && ci < n_chunks && !step(ci, va)) ok = false;
     PIPE_PROF_FLUSH_CONSUMER(w);
     if (sT != nullptr) {
         const float nan = __builtin_nanf("");
