@@ -23,10 +23,11 @@
 //  * Producer waves (8, two per SIMD) build everything that does not depend
 //    on the state, one whole chunk per wave: per-channel decay products with
 //    each lane holding all 16 tokens of its channels, the operand tiles -Kt,
-//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA, and the 16 x 16
-//    unit triangular inverse by back substitution in registers (row
-//    broadcasts by DPP and the gfx950 cross-row lane swaps).  Results go to a
-//    ring of LDS slots.
+//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  The 16 x 16
+//    unit triangular inverses are done in batches of two chunks: the producer
+//    that finishes a batch last solves both by back substitution in
+//    registers, one chunk per pair of 16-lane rows (row broadcasts by DPP).
+//    Results go to a ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
 //    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
@@ -92,6 +93,14 @@ typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
 
 constexpr int kNP = 8;                 // producer waves (two per SIMD)
 constexpr int kRing = 8;               // LDS slots
+#ifndef KDA_PIPE_EARLY
+#define KDA_PIPE_EARLY 0                // producers do the decay arithmetic before taking the slot
+#endif
+#ifndef KDA_PIPE_BATCH
+#define KDA_PIPE_BATCH 2
+#endif
+constexpr int kBatch = KDA_PIPE_BATCH;  // chunks per triangular-inverse batch (2 or 4)
+constexpr int kNBatch = kRing / kBatch; // batches in flight
 constexpr int kSpinLimit = 1 << 17;    // polls (about 128 cycles each) before giving up
 #ifndef KDA_PIPE_SLEEP
 #define KDA_PIPE_SLEEP 2                // s_sleep argument between polls (64 cycles each)
@@ -122,12 +131,18 @@ struct PipeCfg {
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    static constexpr int BYTES = kRing * SLOT;
+    // triangular-inverse batches (chunks kBatch b .. kBatch b + kBatch-1,
+    // kNBatch batches in flight): per chunk the 16 columns of -N (16 floats
+    // each) and beta
+    static constexpr int O_NB = kRing * SLOT;
+    static constexpr int O_BT = O_NB + kRing * 16 * 16 * 4;
+    static constexpr int BYTES = O_BT + kRing * 16 * 4;
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
     static_assert(BYTES <= 160 * 1024 - 256, "LDS budget");
     static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
+    static_assert((kBatch == 2 || kBatch == 4) && kRing % kBatch == 0, "inverse batches cover the ring");
 };
 
 // Position of channel c inside its 32-channel group in the permuted tiles:
@@ -165,18 +180,6 @@ template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
                                                               0x150 + N, 0xF, 0xF, true));
-}
-// The value of row g (lanes 16g .. 16g+15) in every row, for g = 0..3, lane
-// order kept: two gfx950 cross-row swaps produce all four broadcasts.
-__device__ __forceinline__ void all_rows(float x, float (&out)[4]) {
-    const int xi = __builtin_bit_cast(int, x);
-    const auto p16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);   // rows 0022 / 1133
-    const auto e = __builtin_amdgcn_permlane32_swap((int)p16[0], (int)p16[0], false, false);
-    const auto o = __builtin_amdgcn_permlane32_swap((int)p16[1], (int)p16[1], false, false);
-    out[0] = __builtin_bit_cast(float, (int)e[0]);
-    out[1] = __builtin_bit_cast(float, (int)o[0]);
-    out[2] = __builtin_bit_cast(float, (int)e[1]);
-    out[3] = __builtin_bit_cast(float, (int)o[1]);
 }
 // y += (lane M of the row's n) * m, one v_fmac_f32 with a DPP row broadcast
 // on its first source.  The broadcast operand must not be written by a VALU
@@ -238,16 +241,29 @@ __device__ __forceinline__ int flag_load(int* f) {
 __device__ __forceinline__ void flag_store(int* f, int v, int lane) {
     if (lane == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Wait until all N counters f[0..N-1] are >= target (N = 4: one 16-byte
-// read).  Returns false (and raises the workgroup's stop flag) if the wait runs
+// Count a chunk into its inverse batch: returns the count before this one
+// (wave-uniform).  Release: this wave's LDS writes are done before the count;
+// acquire: the wave that counts last sees every writer of the batch.
+__device__ __forceinline__ int batch_count(int* c, int lane) {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Wait until all N counters f[0..N-1] are >= target (N = 4).  Returns false (and raises the workgroup's stop flag) if the wait runs
 // out, or if another wave has raised it.
 template <int N>
 __device__ __forceinline__ bool wait_all_at_least(int* f, int target, int* stop) {
-    static_assert(N == 4, "one 16-byte read of the consumer counters");
+    static_assert(N == 4, "four consumer counters");
     int n = 0;
     for (;;) {
-        const intx4 v = *reinterpret_cast<const volatile intx4*>(f);
-        const int m = __builtin_amdgcn_readfirstlane(min(min(v[0], v[1]), min(v[2], v[3])));
+        // (LDS atomic loads: a volatile vector read through a generic pointer
+        // becomes a flat load, which waits for every global load in flight)
+        const int v0 = __hip_atomic_load(f + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int v1 = __hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int v2 = __hip_atomic_load(f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int v3 = __hip_atomic_load(f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int m = __builtin_amdgcn_readfirstlane(min(min(v0, v1), min(v2, v3)));
         if (m >= target) break;
         if (__builtin_amdgcn_readfirstlane(
                 __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
@@ -293,12 +309,14 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
-    // ready[kRing], released[kRing][NC] (one counter per consumer), stop
-    constexpr int NFLAGS = kRing + kRing * NC + 1;
+    // ready[kRing], released[kRing][NC] (one counter per consumer), stop,
+    // batch[kNBatch] (chunks counted into the inverse batches in flight)
+    constexpr int NFLAGS = kRing + kRing * NC + 1 + kNBatch;
     __shared__ __attribute__((aligned(16))) int flags[NFLAGS];
     int* ready = flags;
     int* released = flags + kRing;
     int* stop = flags + kRing + kRing * NC;
+    int* batch = stop + 1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -329,6 +347,7 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const int64_t t_begin = cu ? (int64_t)cu[seq] : (int64_t)seq * T_len;
     const int64_t t_end = cu ? (int64_t)cu[seq + 1] : t_begin + T_len;
     const int64_t n_chunks = (t_end - t_begin + 15) / 16;
+    const int nch = (int)n_chunks;
 
     if (tid < NFLAGS) flags[tid] = 0;
     __syncthreads();
@@ -344,54 +363,64 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         uint32_t rg[16], rk[16], rq[16];   // CPL bf16 channels per word
         // V slice of the chunk: lane holds token lane/4, columns 16 (lane%4) .. +15
         bf16x8 rv[2];
-        // beta as zero-extended 32-bit words: 16-bit values would be packed in
-        // pairs right after the loads, which makes the wave wait for them
-        uint32_t rbl, rb4[4];
+        // beta of token lr as a zero-extended 32-bit word (16-bit values would
+        // be packed in pairs right after the loads, which makes the wave wait)
+        uint32_t rbl;
         const int g_row = H * DK * 2, kv_row = (int)(stride * 2), b_row = H * 2;
         const int vt = lane >> 2, vc = 16 * (lane & 3);
         auto load_word = [](rsrc_t r, int off) -> uint32_t {
             if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
             else return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
         };
-        // Loads of chunk ci.  Past the last chunk the resources cover no bytes
-        // and the loads return zeros; they are issued anyway, so that every
-        // iteration issues the same memory operations and no register copy
-        // has to wait for loads still in flight.
-        auto issue_loads = [&](int64_t ci) {
-            const int64_t t0 = t_begin + ci * 16;
+        // Loads of chunk ci (g, k, q, beta; V separately).  Past the last chunk
+        // the resources cover no bytes and the loads return zeros; they are
+        // issued anyway, so that every iteration issues the same memory
+        // operations and no register copy has to wait for loads in flight.
+        auto chunk_rows = [&](int64_t ci, int64_t& t0) -> int {
+            t0 = t_begin + ci * 16;
             const int64_t rem = t_end - t0;
-            const int valid = (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
+            return (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
+        };
+        auto issue_gkq = [&](int64_t ci) {
+            int64_t t0;
+            const int valid = chunk_rows(ci, t0);
             const rsrc_t r_g = make_rsrc(g + (t0 * H + head) * DK, (uint32_t)(valid * g_row));
             const rsrc_t r_k = make_rsrc(k + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
             const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
-            const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 rg[t] = load_word(r_g, t * g_row + c0 * 2);
                 rk[t] = load_word(r_k, t * kv_row + c0 * 2);
                 rq[t] = load_word(r_q, t * kv_row + c0 * 2);
             }
-            rv[0] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2);
-            rv[1] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2 + 16);
             const rsrc_t r_b = make_rsrc(beta + t0 * H + head, (uint32_t)(valid * b_row));
             rbl = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, lr * b_row, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                rb4[i] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, (4 * lq + i) * b_row, 0, 0);
+        };
+        auto issue_v = [&](int64_t ci) {
+            int64_t t0;
+            const int valid = chunk_rows(ci, t0);
+            const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
+            rv[0] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2);
+            rv[1] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2 + 16);
         };
         // channel j of a word as fp32 (bf16 is the top half of an fp32)
         auto chan = [](uint32_t w, int j) -> float {
             return __builtin_bit_cast(float, j == 0 ? w << 16 : w & 0xffff0000u);
         };
-        // CPL bf16 values as one word / half-word LDS store
-        auto put = [](char* p, const float (&x)[CPL]) {
-            if constexpr (CPL == 2) {
-                *reinterpret_cast<bf16x2*>(p) = bf16x2{(__bf16)x[0], (__bf16)x[1]};
-            } else {
-                *reinterpret_cast<__bf16*>(p) = (__bf16)x[0];
-            }
+        // CPL fp32 values as CPL packed bf16 (the low half first), and their
+        // one-word / half-word LDS store
+        auto pack = [](const float (&x)[CPL]) -> uint32_t {
+            if constexpr (CPL == 2)
+                return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{x[0], x[1]}, bf16x2));
+            else
+                return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x[0]);
         };
-        issue_loads(pw);
+        auto put = [](char* p, uint32_t w) {
+            if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(p) = w;
+            else *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+        };
+        issue_gkq(pw);
+        issue_v(pw);
         PIPE_PROF_INIT();
 
         // The loop has no early exit: an exit path would merge with the
@@ -403,15 +432,15 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int64_t ci = pw; ci < n_chunks;) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
-            const bool go = wait_all_at_least<NC>(&released[s * NC], round, stop);
-            char* slot = smem + s * SLOT;
-            PIPE_PROF_MARK(0);
             PIPE_PROF_VMWAIT(5);
+            bool go = true;
+            if (!KDA_PIPE_EARLY) go = wait_all_at_least<NC>(&released[s * NC], round, stop);
 
-            // ---- decay products ---------------------------------------------
+            // ---- decay products, in registers -------------------------------
             // a_t = e^{g_t}; F_t = e^{G_t} = a_0 .. a_t (forward), then
             // E_t = e^{-G_t} = e^{-G_15} a_{t+1} .. a_15 (backward)
             float a[CPL][16], F[CPL];
+            uint32_t wkt[16], wqt[16], wki[16];   // packed bf16 tile words per token
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 float kt[CPL], qt[CPL];
@@ -422,8 +451,8 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     kt[j] = -(chan(rk[t], j) * F[j]);   // stored negated: -K e^G
                     qt[j] = chan(rq[t], j) * F[j];
                 }
-                put(slot + Cfg::O_KT + t * PK + pos * 2, kt);
-                put(slot + Cfg::O_QT + t * PK + pos * 2, qt);
+                wkt[t] = pack(kt);
+                wqt[t] = pack(qt);
             }
             float E[CPL];
 #pragma unroll
@@ -436,7 +465,35 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                     if (t < 15) E[j] *= a[j][t + 1];
                     ki[j] = chan(rk[t], j) * E[j];
                 }
-                put(slot + Cfg::O_KI + t * PH + c0 * 2, ki);
+                wki[t] = pack(ki);
+            }
+            // beta to fp32 before the next chunk's loads reuse its registers
+            // (a conversion sunk below them would keep both copies live and
+            // add a register move that waits for the loads)
+            float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
+            asm volatile("" : "+v"(bl));
+            // with the arithmetic ahead of the wait, the tile words are
+            // computed here (the compiler would otherwise sink it to the stores)
+            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wkt[0]), "v"(wkt[1]), "v"(wkt[2]), "v"(wkt[3]), "v"(wkt[4]), "v"(wkt[5]),
+                         "v"(wkt[6]), "v"(wkt[7]), "v"(wkt[8]), "v"(wkt[9]), "v"(wkt[10]), "v"(wkt[11]),
+                         "v"(wkt[12]), "v"(wkt[13]), "v"(wkt[14]), "v"(wkt[15]));
+            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wqt[0]), "v"(wqt[1]), "v"(wqt[2]), "v"(wqt[3]), "v"(wqt[4]), "v"(wqt[5]),
+                         "v"(wqt[6]), "v"(wqt[7]), "v"(wqt[8]), "v"(wqt[9]), "v"(wqt[10]), "v"(wqt[11]),
+                         "v"(wqt[12]), "v"(wqt[13]), "v"(wqt[14]), "v"(wqt[15]));
+            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wki[0]), "v"(wki[1]), "v"(wki[2]), "v"(wki[3]), "v"(wki[4]), "v"(wki[5]),
+                         "v"(wki[6]), "v"(wki[7]), "v"(wki[8]), "v"(wki[9]), "v"(wki[10]), "v"(wki[11]),
+                         "v"(wki[12]), "v"(wki[13]), "v"(wki[14]), "v"(wki[15]), "v"(F[0]), "v"(F[CPL - 1]));
+            PIPE_PROF_MARK(1);
+
+            // ---- into the slot -----------------------------------------------
+            if (KDA_PIPE_EARLY) go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+            char* slot = smem + s * SLOT;
+            PIPE_PROF_MARK(0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
+                put(slot + Cfg::O_QT + t * PK + pos * 2, wqt[t]);
+                put(slot + Cfg::O_KI + t * PH + c0 * 2, wki[t]);
             }
             // e^{G_15} per channel, laid out for the consumers' row
             // broadcasts: channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2]
@@ -448,21 +505,9 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             }
             *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
             *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
-            // beta to fp32 before the next chunk's loads reuse its registers
-            // (a conversion sunk below them would keep both copies live and
-            // add a register move that waits for the loads)
-            float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
-            asm volatile("" : "+v"(bl));
-            float b4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b4[i] = __builtin_bit_cast(float, rb4[i] << 16);
-                asm volatile("" : "+v"(b4[i]));
-            }
-            PIPE_PROF_MARK(1);
-
-            // the next chunk of this wave streams in while this one finishes
-            issue_loads(ci + kNP);
+            // the next chunk of this wave streams in from here on
+            issue_gkq(ci + kNP);
+            issue_v(ci + kNP);
             PIPE_PROF_MARK(2);
 
             // ---- A_kk^T, A_qk^T (16x16x32 MFMA over the key channels) -------
@@ -487,31 +532,66 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                       4 * lq + 2 <= lr ? aqk[2] : 0.f, 4 * lq + 3 <= lr ? aqk[3] : 0.f);
             PIPE_PROF_MARK(3);
 
-            // ---- Y = (I + N)^{-1}, N = (diag(beta) A_kk)^T strictly upper ----
-            // -N[4q+i][r] = -beta_r A_kk[r][4q+i] sits in lane (q, r); spread
-            // every row of it to all four lane rows, then back-substitute.
-            float np[16], y[16];
+            // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk, in batches ------------
+            // This chunk's part: column c = lr of -N holds -beta_c A_kk[c][r]
+            // for r < c; lane (q, c) has rows r = 4q+i (the tile holds -Kt, so
+            // akk[i] = -A_kk[c][4q+i]).  It waits in LDS, with beta, until the
+            // last chunk of its batch to get here inverts the whole batch, one
+            // chunk per 4/kBatch of the 16-lane rows (the row broadcasts of the
+            // back substitution stay inside a row), so fewer rows repeat work.
+            constexpr int RPC = 4 / kBatch;   // lane rows per chunk
+            const int cix = (int)ci;
+            const int bt = cix / kBatch, bslot = bt % kNBatch;
+            float* nbp = reinterpret_cast<float*>(smem + Cfg::O_NB);
+            float* btp = reinterpret_cast<float*>(smem + Cfg::O_BT);
+            const int mine = bslot * kBatch + cix % kBatch;   // this chunk's buffer
+            *reinterpret_cast<floatx4*>(nbp + (mine * 16 + lr) * 16 + 4 * lq) =
+                floatx4{4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
+                        4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
+            if (lq == 0) btp[mine * 16 + lr] = bl;
+            // chunks of the batch, and the count of this buffer's earlier
+            // batches (all full: only the last batch can be short)
+            const int n_in = nch - kBatch * bt < kBatch ? nch - kBatch * bt : kBatch;
+            const int counted = go ? batch_count(&batch[bslot], lane) : -1;
+            if (counted == kBatch * (bt / kNBatch) + n_in - 1) {
+                // lane (row, c): chunk kBatch bt + row / RPC, column c of -N,
+                // then of Y - I
+                const int gi = lq / RPC;
+                float np[16], y[16];
+                const float* col = nbp + ((bslot * kBatch + gi) * 16 + lr) * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float rows[4];
-                all_rows((4 * lq + i < lr) ? bl * akk[i] : 0.f, rows);
+                for (int j = 0; j < 4; ++j) {
+                    const floatx4 v4 = *reinterpret_cast<const floatx4*>(col + 4 * j);
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) np[4 * g4 + i] = rows[g4];
+                    for (int e = 0; e < 4; ++e) np[4 * j + e] = v4[e];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[r] = np[r];
+                back_subst(y, np);
+                // M'[r][4q+e] = (Y[4q+e][r] + delta) beta_{4q+e}, lane (q, r) of
+                // the chunk's 16x16x16 A operand; this lane holds column r = lr
+                // (the first lane row of each chunk writes it)
+                const int cg = kBatch * bt + gi;
+                const bool writer = lq % RPC == 0 && gi < n_in;
+                if (writer) {
+                    char* slot_g = smem + (cg % kRing) * SLOT;
+                    const float* bet = btp + (bslot * kBatch + gi) * 16;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const floatx4 bq = *reinterpret_cast<const floatx4*>(bet + 4 * q4);
+                        float ye[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ye[e] = (y[4 * q4 + e] + (4 * q4 + e == lr ? 1.f : 0.f)) * bq[e];
+                        *reinterpret_cast<shortx4*>(slot_g + Cfg::O_MP + (16 * q4 + lr) * 8) =
+                            pack4(ye[0], ye[1], ye[2], ye[3]);
+                    }
+                }
+                // publish the batch's chunks, one lane per chunk, after the
+                // M' writes (the release waits for them)
+                if (writer && lr == 0)
+                    __hip_atomic_store(&ready[cg % kRing], cg / kRing + 1, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[r] = np[r];
-            back_subst(y, np);
-            // M'[r][4q+e] = X[r][4q+e] beta[4q+e], X = Y^T: lane (q, r) takes
-            // y[4q+e] plus the identity
-            float ye[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ye[e] = (lq == 0 ? y[e] : lq == 1 ? y[4 + e] : lq == 2 ? y[8 + e] : y[12 + e]) +
-                        (4 * lq + e == lr ? 1.f : 0.f);
-            *reinterpret_cast<shortx4*>(slot + Cfg::O_MP + lane * 8) =
-                pack4(ye[0] * b4[0], ye[1] * b4[1], ye[2] * b4[2], ye[3] * b4[3]);
-
-            flag_store(&ready[s], round + 1, go ? lane : 1);
             PIPE_PROF_MARK(4);
             ci = go ? ci + kNP : n_chunks;
         }
@@ -560,7 +640,6 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     shortx4 ident;
 #pragma unroll
     for (int e = 0; e < 4; ++e) ident[e] = lr == 4 * lq + e ? (short)0x3F80 : (short)0;
-    const int nch = (int)n_chunks;
     bool ok = nch == 0 || wait_at_least(&ready[0], 1, stop);
     // the slot is read only after its counter was seen (the compiler keeps
     // the reads below this point; the LDS serves a wave's operations in order)
