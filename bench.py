@@ -141,8 +141,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA mixer here is a single-GPU library "
-              f"(requested --gpus {args.gpus}); see the sharding notes in the design document.",
-              file=sys.stderr, flush=True)
+              f"(requested --gpus {args.gpus}). Across GPUs the heads would be split (each "
+              f"rank owns whole heads and their states), which needs no collective inside "
+              f"the mixer.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch
