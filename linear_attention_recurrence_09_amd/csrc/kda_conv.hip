@@ -7,11 +7,13 @@
 // rolling state of a sequence is its last 3 raw inputs per channel.  KDA
 // one-head diagram: q and k are then L2-normalised over the 128-d head.
 //
-// HBM-bound stencil: read x once (plus a 3-token halo per tile) and write y
+// HBM-bound stencil: read x once (plus a 3-token halo per strip) and write y
 // once.  A thread owns 8 consecutive channels (one 16-byte bf16 vector) for a
-// tile of kTile tokens and slides the 3-value window in registers; D/8 lanes
-// of one head reduce the sum of squares with xor shuffles.  A block covers
-// 2048 channels; windows restart at every sequence start.
+// strip of tokens (128 in bf16), streamed in groups: the next group's rows are
+// loaded while the current group is computed, and the 3-value window slides
+// in registers across groups, so weights and halo are loaded once per strip.
+// D/8 lanes of one head reduce the sum of squares with xor shuffles.  A block
+// covers 2048 channels; windows restart at every sequence start.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -21,10 +23,15 @@ namespace {
 
 constexpr int kConvThreads = 256;
 constexpr int kConvChannels = kConvThreads * 8;
-// tokens per thread: all of a tile's inputs (plus the 3-token halo) are loaded
-// before any arithmetic, so a thread keeps TT + 3 16-byte loads in flight
+// Tokens per block (TT) and per streamed group (G).  A block walks its strip
+// of TT tokens in groups of G: the next group's rows are in flight while the
+// current group is computed, and the 3-token window slides across groups, so
+// the weights and the halo are loaded once per strip.
 template <typename T>
-struct ConvTile { static constexpr int TT = sizeof(T) == 2 ? 16 : 8; };
+struct ConvTile {
+    static constexpr int TT = sizeof(T) == 2 ? 128 : 8;
+    static constexpr int G = sizeof(T) == 2 ? 16 : 8;
+};
 
 struct SeqRange {
     int s;
@@ -83,12 +90,22 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kConvThreads)
 conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ y,
             const T* __restrict__ state_in, const int32_t* __restrict__ cu, int num_seqs,
-            int T_len, int64_t N, int P, int HD, float l2_eps) {
+            int T_len, int64_t N, int P, int HD, float l2_eps, int tiles, int tiles_per_xcd,
+            int cblocks) {
     constexpr int TT = ConvTile<T>::TT;
     using Raw8 = typename RawVec<T, 8>::type;
-    const int c0 = blockIdx.y * kConvChannels + threadIdx.x * 8;
+    // Block -> (token tile, channel block).  Blocks go to the 8 XCDs round
+    // robin, so XCD k gets the blocks k, k+8, ...: they are given a contiguous
+    // range of tiles, every channel block of a tile before the next tile.  A
+    // tile's 3-token halo was then read shortly before on the same XCD and is
+    // served from its L2.
+    const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
+    const int tile = xcd * tiles_per_xcd + li / cblocks;
+    if (tile >= tiles) return;
+    const int cbase = (li % cblocks) * kConvChannels;   // the block's first channel
+    const int c0 = cbase + threadIdx.x * 8;
     const bool active = c0 < P;
-    const int64_t t0 = (int64_t)blockIdx.x * TT;
+    const int64_t t0 = (int64_t)tile * TT;
     const int64_t t1 = t0 + TT < N ? t0 + TT : N;
     const bool is_qk = c0 < 2 * HD;   // uniform over the D/8 lanes of a head
 
@@ -100,46 +117,66 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
 
     SeqRange sr = find_seq(cu, num_seqs, T_len, t0);
 
-    // Fast path (uniform over the block): the tile and its halo lie inside one
+    // Fast path (uniform over the block): the strip and its halo lie inside one
     // sequence, so every window reads plain inputs.
     if (sr.start <= t0 - 3 && sr.end >= t0 + TT) {
-        const int cl = active ? c0 : 0;
-        Raw8 raw[TT + 3];
-#pragma unroll
-        for (int j = 0; j < TT + 3; ++j)
-            raw[j] = *reinterpret_cast<const Raw8*>(x + (t0 - 3 + j) * P + cl);
+        constexpr int G = ConvTile<T>::G, NG = TT / G;
+        static_assert(TT % G == 0, "whole groups per strip");
+        // rows t0-3 .. of this strip from the block's first channel (a
+        // wave-uniform resource; the lane's channels go in the offset).  The
+        // range ends with the strip, so the prefetch past the last group and
+        // lanes past the last channel read zeros.
+        const int64_t rows = N - (t0 - 3) < TT + 3 ? N - (t0 - 3) : TT + 3;
+        const int row_bytes = P * (int)sizeof(T);
+        const rsrc_t rx = make_rsrc(x + (t0 - 3) * P + cbase,
+                                    (uint32_t)(rows * row_bytes - (int64_t)cbase * (int)sizeof(T)));
+        const int lane_off = (int)threadIdx.x * 8 * (int)sizeof(T);
         float win[8][3];
-        {
-            float v0[8], v1[8], v2[8];
-            RawVec<T, 8>::unpack(raw[0], v0);
-            RawVec<T, 8>::unpack(raw[1], v1);
-            RawVec<T, 8>::unpack(raw[2], v2);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { win[e][0] = v0[e]; win[e][1] = v1[e]; win[e][2] = v2[e]; }
+        for (int j = 0; j < 3; ++j) {
+            float v[8];
+            RawVec<T, 8>::unpack(BufLoad<T, 8>::load(rx, j * row_bytes + lane_off), v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[e][j] = v[e];
         }
+        auto load_group = [&](Raw8 (&r)[G], int grp) {
 #pragma unroll
-        for (int j = 0; j < TT; ++j) {
-            float xv[8], out[8];
-            RawVec<T, 8>::unpack(raw[j + 3], xv);
-            float ss = 0.f;
+            for (int j = 0; j < G; ++j) r[j] = BufLoad<T, 8>::load(rx, (3 + grp * G + j) * row_bytes + lane_off);
+        };
+        auto run_group = [&](const Raw8 (&r)[G], int grp) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pre = wt[e][0] * win[e][0] + wt[e][1] * win[e][1] +
-                                  wt[e][2] * win[e][2] + wt[e][3] * xv[e];
-                out[e] = siluf_(pre);
-                ss += out[e] * out[e];
-                win[e][0] = win[e][1];
-                win[e][1] = win[e][2];
-                win[e][2] = xv[e];
+            for (int j = 0; j < G; ++j) {
+                float xv[8], out[8];
+                RawVec<T, 8>::unpack(r[j], xv);
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pre = wt[e][0] * win[e][0] + wt[e][1] * win[e][1] +
+                                      wt[e][2] * win[e][2] + wt[e][3] * xv[e];
+                    out[e] = siluf_(pre);
+                    ss += out[e] * out[e];
+                    win[e][0] = win[e][1];
+                    win[e][1] = win[e][2];
+                    win[e][2] = xv[e];
+                }
+                ss = group_sum<D / 8>(ss);
+                if (is_qk) {
+                    const float inv = rsqrt_nr(ss + l2_eps);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[e] *= inv;
+                }
+                if (active) store8_nt(y + (t0 + grp * G + j) * P + c0, out);
             }
-            ss = group_sum<D / 8>(ss);
-            if (is_qk) {
-                const float inv = rsqrt_nr(ss + l2_eps);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) out[e] *= inv;
-            }
-            if (active) store8_nt(y + (t0 + j) * P + c0, out);
+        };
+        Raw8 ra[G], rb[G];
+        load_group(ra, 0);
+        for (int pr = 0; pr < NG / 2; ++pr) {
+            load_group(rb, 2 * pr + 1);
+            run_group(ra, 2 * pr);
+            load_group(ra, 2 * pr + 2);   // past the strip on the last pair: zeros
+            run_group(rb, 2 * pr + 1);
         }
+        if constexpr (NG % 2 == 1) run_group(ra, NG - 1);
         return;
     }
 
@@ -250,10 +287,13 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
     const unsigned cblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
     if (N > 0) {
         constexpr int TT = ConvTile<T>::TT;
-        const unsigned tiles = (unsigned)((N + TT - 1) / TT);
-        hipLaunchKernelGGL((conv_kernel<T, D>), dim3(tiles, cblocks), dim3(kConvThreads), 0, s,
+        const int64_t tiles = (N + TT - 1) / TT;
+        const int64_t per_xcd = (tiles + 7) / 8;
+        const int64_t blocks = 8 * per_xcd * cblocks;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((conv_kernel<T, D>), dim3((unsigned)blocks), dim3(kConvThreads), 0, s,
                            (const T*)x, w, (T*)y, (const T*)state_in, cu, num_seqs, T_len, N, P,
-                           H * D, l2_eps);
+                           H * D, l2_eps, (int)tiles, (int)per_xcd, (int)cblocks);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
