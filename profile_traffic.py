@@ -3,7 +3,9 @@
 Inputs (CSV files written by the commands recorded in the summaries):
   --trace  <dir>/bench_kernel_stats.csv   from
            rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- \
-               python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
+               python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline
+           (the per-dispatch <dir>/bench_kernel_trace.csv beside it gives the
+           average over the timed steps, the last 10 chunk-kernel dispatches)
   --fetch  <dir>/fetch_counter_collection.csv from
            rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters
   --write  <dir>/write_counter_collection.csv from
@@ -55,13 +57,22 @@ def main():
     lines = ["# rocprofv3 kernel statistics of one bench.py run (prefill T=65536, H=96, D=128,",
              "# bf16 I/O; decode B=256 x 64 steps), MI355X",
              "# command: rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- "
-             "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline",
+             "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
              f"{'kernel':60s} {'calls':>6s} {'avg_ms':>10s} {'min_ms':>10s} {'max_ms':>10s} {'pct':>6s}"]
     for r in rows:
         lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e6:10.4f} "
                      f"{float(r['MinNs'])/1e6:10.4f} {float(r['MaxNs'])/1e6:10.4f} "
                      f"{float(r['Percentage']):6.2f}")
     chunk_avg = [float(r["AverageNs"]) / 1e6 for r in rows if CHUNK_TAG in r["Name"]]
+    # per dispatch: the timed steps are the last STEPS chunk-kernel launches
+    STEPS = 10
+    ktrace = os.path.join(os.path.dirname(args.trace), "bench_kernel_trace.csv")
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+            for r in csv.DictReader(open(ktrace)) if CHUNK_TAG in r["Kernel_Name"]]
+    timed_avg = statistics.mean(durs[-STEPS:]) if len(durs) >= STEPS else None
+    lines += ["", f"# chunk kernel per dispatch (ms): {' '.join(f'{d:.3f}' for d in durs)}",
+              f"# chunk kernel average over the {STEPS} timed steps: "
+              + (f"{timed_avg:.4f} ms" if timed_avg else "n/a")]
 
     # byte counters
     fetch = per_dispatch(args.fetch, "FETCH_SIZE")
@@ -95,6 +106,7 @@ def main():
         "algorithmic_bytes_per_launch": algo,
         "traffic_over_algorithmic": (fb + wb) / algo,
         "kernel_trace_avg_ms": chunk_avg[0] if chunk_avg else None,
+        "kernel_trace_timed_avg_ms": timed_avg,
     }
     lines += ["",
               "# HBM bytes of the chunk kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
