@@ -149,6 +149,10 @@ CHUNK_CASES = [
     ("bf16", 128, 2, [0, 5, 64, 130, 1, 0, 65], True, 16, True, -0.05),
     ("bf16", 128, 2, [100, 100, 100], False, 16, False, -5.0),
     ("bf16", 128, 2, [2000], False, 16, True, -0.05),
+    # sequences of 2, 3, 2, 6, 8, 16 and 3 chunks: full and short last pairs of
+    # the two-chunk inverse batches, and lengths that are exact multiples of 16
+    ("bf16", 128, 2, [32, 48, 17, 96, 128, 256, 33], True, 16, True, -5.0),
+    ("bf16", 64, 2, [16, 31, 80, 240], True, 16, False, -0.05),
     # 32 sequences x 8 heads = 256 chains: takes the full 128-column slices
     ("bf16", 128, 8, [int(v) for v in np.random.default_rng(5).integers(1, 150, 32)], True, 64,
      True, -0.05),
