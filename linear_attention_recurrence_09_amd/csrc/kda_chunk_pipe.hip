@@ -141,7 +141,9 @@ struct PipeCfg {
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
     static_assert(BYTES <= 160 * 1024 - 256, "LDS budget");
-    static_assert((kRing & (kRing - 1)) == 0, "ring size is a power of two");
+    // every producer keeps one slot (rings whose size does not divide the
+    // producer count gave wrong results in tests)
+    static_assert(kNP % kRing == 0, "ring size divides the producer count");
     static_assert((kBatch == 2 || kBatch == 4) && kRing % kBatch == 0, "inverse batches cover the ring");
 };
 
@@ -568,9 +570,9 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) y[r] = np[r];
                 back_subst(y, np);
-                // M'[r][4q+e] = (Y[4q+e][r] + delta) beta_{4q+e}, lane (q, r) of
-                // the chunk's 16x16x16 A operand; this lane holds column r = lr
-                // (the first lane row of each chunk writes it)
+                // M'[r][4q+e] = Y[4q+e][r] beta_{4q+e}, lane (q, r) of the
+                // chunk's 16x16x16 A operand; this lane holds column r = lr of
+                // Y - I (the first lane row of each chunk writes it)
                 const int cg = kBatch * bt + gi;
                 const bool writer = lq % RPC == 0 && gi < n_in;
                 if (writer) {
@@ -579,12 +581,15 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         const floatx4 bq = *reinterpret_cast<const floatx4*>(bet + 4 * q4);
-                        float ye[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ye[e] = (y[4 * q4 + e] + (4 * q4 + e == lr ? 1.f : 0.f)) * bq[e];
                         *reinterpret_cast<shortx4*>(slot_g + Cfg::O_MP + (16 * q4 + lr) * 8) =
-                            pack4(ye[0], ye[1], ye[2], ye[3]);
+                            pack4(y[4 * q4] * bq[0], y[4 * q4 + 1] * bq[1], y[4 * q4 + 2] * bq[2],
+                                  y[4 * q4 + 3] * bq[3]);
                     }
+                    // the unit diagonal: entry lr of y is exactly 0 (a column
+                    // of Y - I has nothing on or below the diagonal), so
+                    // M'[lr][lr] = beta_lr goes in with one 2-byte write
+                    *reinterpret_cast<__bf16*>(slot_g + Cfg::O_MP + (16 * (lr >> 2) + lr) * 8 + (lr & 3) * 2) =
+                        (__bf16)bet[lr];
                 }
                 // publish the batch's chunks, one lane per chunk, after the
                 // M' writes (the release waits for them)
