@@ -95,6 +95,16 @@ def decode_bytes(B, H, D, es=2):
             + P * 4 * 4)                 # conv weights
 
 
+def decode_multi_bytes(B, K, H, D, es=2, write_states=True, outputs=True):
+    """Algorithmic HBM bytes of one kda_decode_multi call of K tokens."""
+    P = 3 * H * D
+    states = B * H * D * D * 4 + B * P * 3 * es
+    return ((2 if write_states else 1) * states
+            + B * K * (P * es + H * D * es + H * es)   # x, g, beta
+            + (B * K * H * D * es if outputs else 0)   # o
+            + P * 4 * 4)                               # conv weights
+
+
 def cpu_baseline(inp, spec, T_s, H_s):
     """Oracle on the first T_s tokens of the first H_s heads (all its threads)."""
     import numpy as np
@@ -286,6 +296,70 @@ def main():
                             "tokens_per_s": B / (med * 1e-3),
                             "hbm_frac": db / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
         log(f"decode: {med:.3f} ms/step, {result['decode']['TBps']:.2f} TB/s")
+
+        # K tokens per call (checking drafted tokens): the same 64 tokens per
+        # sequence as 64 / K calls, states in place, every token accepted
+        per_k = {}
+        for K in (2, 4, 8):
+            calls = steps // K
+            blk = [(d["x"][c * K:(c + 1) * K].transpose(0, 1).contiguous(),
+                    d["g"][c * K:(c + 1) * K].transpose(0, 1).contiguous(),
+                    d["beta"][c * K:(c + 1) * K].transpose(0, 1).contiguous())
+                   for c in range(calls)]
+            om = torch.empty((B, K, Hd, Dd), dtype=d["x"].dtype, device="cuda")
+
+            def multi_pass(cs, S, events=None):
+                for c, (xb, gb, bb) in enumerate(blk):
+                    if events:
+                        events[c][0].record(stream)
+                    kda.kda_decode_multi(xb, d["conv_w"], cs, gb, bb, S, B, K, Hd, Dd, o=om,
+                                         conv_state_out=cs, state_out=S, stream=stream)
+                    if events:
+                        events[c][1].record(stream)
+
+            multi_pass(d["conv_state"].clone(), d["S0"].clone())
+            cs, S = d["conv_state"].clone(), d["S0"].clone()
+            mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(calls)]
+            torch.cuda.synchronize()
+            multi_pass(cs, S, mev)
+            torch.cuda.synchronize()
+            per = sorted(e[0].elapsed_time(e[1]) for e in mev)
+            med = per[len(per) // 2]
+            mb = decode_multi_bytes(B, K, Hd, Dd)
+            per_k[str(K)] = {"calls": calls, "ms_per_call_median": med, "ms_per_call_min": per[0],
+                             "ms_per_call_max": per[-1], "bytes_per_call": mb,
+                             "TBps": mb / (med * 1e-3) / 1e12,
+                             "tokens_per_s": B * K / (med * 1e-3),
+                             "hbm_frac": mb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            log(f"decode_multi K={K}: {med:.3f} ms/call, {B * K / med:.0f}k tokens/s")
+            del blk, om
+        # the check-then-accept pair at K = 4: outputs only, then the accepted
+        # tokens (all four, the most state work) in place
+        K = 4
+        xb, gb, bb = (d[n][:K].transpose(0, 1).contiguous() for n in ("x", "g", "beta"))
+        om = torch.empty((B, K, Hd, Dd), dtype=d["x"].dtype, device="cuda")
+        acc = torch.full((B,), K, dtype=torch.int32, device="cuda")
+        cs, S = d["conv_state"].clone(), d["S0"].clone()
+        pair_ms = []
+        for rep in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kda.kda_decode_multi(xb, d["conv_w"], cs, gb, bb, S, B, K, Hd, Dd, o=om, stream=stream)
+            kda.kda_decode_multi(xb, d["conv_w"], cs, gb, bb, S, B, K, Hd, Dd, conv_state_out=cs,
+                                 state_out=S, n_tokens=acc, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                pair_ms.append(e0.elapsed_time(e1))
+        pair_ms.sort()
+        pmed = pair_ms[len(pair_ms) // 2]
+        result["decode_multi"] = {
+            "workload": f"{dspec.name}: K tokens per call, states in place",
+            "B": B, "per_K": per_k,
+            "check_then_accept_K4": {
+                "ms_median": pmed, "tokens_per_s": B * K / (pmed * 1e-3),
+                "bytes": decode_multi_bytes(B, K, Hd, Dd, write_states=False)
+                         + decode_multi_bytes(B, K, Hd, Dd, outputs=False)}}
         del d, cs, S
 
     if not args.no_cpu_baseline:

@@ -145,6 +145,43 @@ int kda_decode_step(const void* x, const float* w, void* conv_state, const void*
                     int32_t dtype, float l2_eps, hipStream_t s);
 
 /*
+ * kda_decode_multi -- K new tokens for each of B sequences in one pass over
+ * the states: the check of K drafted tokens in speculative decoding ("Kimi
+ * K3" on archdiff.com, component list: the MTP layer used as an EAGLE-3
+ * drafter, and speculative decoding by MTP self-drafting).  Token t of
+ * sequence b is exactly the step of kda_decode_step applied after tokens
+ * 0 .. t-1 of the same sequence.
+ *
+ *   x               [B, K, 3*H*D]  projected new tokens (before the conv)
+ *   w               [3*H*D, 4]     fp32 filter banks, as in kda_conv
+ *   conv_state_in   [B, 3*H*D, 3]  rolling raw inputs before token 0
+ *   g               [B, K, H, D]   log-decay (clamped to [-5, 0])
+ *   beta            [B, K, H]
+ *   state_in        [B, H, D, D]   fp32 recurrent state before token 0
+ *   n_tokens        [B] int32 on the device, or NULL (= K for every
+ *                   sequence): how many leading tokens of sequence b the output
+ *                   states take in; values are clamped to [0, K]
+ *   state_out       [B, H, D, D]   fp32 state after n_tokens[b] tokens
+ *   conv_state_out  [B, 3*H*D, 3]  rolling raw inputs after n_tokens[b] tokens
+ *   o               [B, K, H, D]   S_t^T q_t for all K tokens, or NULL
+ *
+ * state_out and conv_state_out are both given or both NULL (NULL: outputs
+ * only, nothing is written back).  Each output state is either exactly its
+ * input (in place) or disjoint from every other tensor; o overlaps nothing.
+ * With o NULL only the first n_tokens[b] tokens are processed.  Rollback after
+ * a check: call once with the states NULL (outputs only), then once more with
+ * o NULL, n_tokens = the accepted counts and the states in place.  The state
+ * is read once per call and written at most once.  1 <= K <= 64; a larger K
+ * is KDA_ERR_UNSUPPORTED.
+ */
+#define KDA_DECODE_MULTI_MAX_K 64
+int kda_decode_multi(const void* x, const float* w, const void* conv_state_in,
+                     void* conv_state_out, const void* g, const void* beta,
+                     const float* state_in, float* state_out, void* o, const int32_t* n_tokens,
+                     int32_t B, int32_t K, int32_t H, int32_t D, int32_t dtype, float l2_eps,
+                     hipStream_t s);
+
+/*
  * kda_gated_norm -- head RMSNorm times a full-rank sigmoid gate.
  * ("Inside Kimi K3", KDA one-head diagram: head RMSNorm and sigmoid gate.)
  *   y[t,h,d] = o[t,h,d] / sqrt(mean_d o[t,h,d]^2 + eps) * weight[d]

@@ -43,7 +43,10 @@ def lib():
                                         i32, i32, i32, i32, i32, vp]
         L.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f, vp]
         L.kda_gated_norm.argtypes = [vp, vp, vp, vp, i64, i32, i32, f, i32, vp]
-        for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm"):
+        L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                       i32, f, vp]
+        for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
+                     "kda_decode_multi"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,6 +143,23 @@ def kda_decode_step(x, w, conv_state, g, beta, state, o, B, H, D, l2_eps=1e-6, s
            lib().kda_decode_step(_ptr(x), _ptr(w), _ptr(conv_state), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(o), B, H, D, _dtype(x), l2_eps,
                                  _stream(stream)))
+
+
+def kda_decode_multi(x, w, conv_state_in, g, beta, state_in, B, K, H, D, o=None,
+                     conv_state_out=None, state_out=None, n_tokens=None, l2_eps=1e-6,
+                     stream=None):
+    """K new tokens per sequence in one pass over the states (checking drafted
+    tokens).  x [B, K, 3HD], g [B, K, H, D], beta [B, K, H]; o [B, K, H, D] or
+    None; the output states take in the first n_tokens[b] tokens (None: K)."""
+    _same_dtype(x, conv_state_in, g, beta, *(t for t in (o, conv_state_out) if t is not None))
+    _f32(w, state_in, *(t for t in (state_out,) if t is not None))
+    if n_tokens is not None and n_tokens.dtype != torch.int32:
+        raise TypeError("n_tokens must be int32")
+    _check("kda_decode_multi",
+           lib().kda_decode_multi(_ptr(x), _ptr(w), _ptr(conv_state_in), _ptr(conv_state_out),
+                                  _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                  _ptr(n_tokens), B, K, H, D, _dtype(x), l2_eps,
+                                  _stream(stream)))
 
 
 def kda_gated_norm(o, gate, weight, y, n_tokens, H, D, eps=1e-6, stream=None):

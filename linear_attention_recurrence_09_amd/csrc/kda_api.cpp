@@ -188,6 +188,68 @@ int kda_decode_step(const void* x, const float* w, void* conv_state, const void*
                       fn);
 }
 
+int kda_decode_multi(const void* x, const float* w, const void* conv_state_in,
+                     void* conv_state_out, const void* g, const void* beta,
+                     const float* state_in, float* state_out, void* o, const int32_t* n_tokens,
+                     int32_t B, int32_t K, int32_t H, int32_t D, int32_t dtype, float l2_eps,
+                     hipStream_t s) {
+    const char* fn = "kda_decode_multi";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+    if (K < 1) return fail(KDA_ERR_INVALID_ARG, "%s: K must be >= 1 (got %d)", fn, K);
+    if (K > KDA_DECODE_MULTI_MAX_K)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: K must be <= %d (got %d)", fn, KDA_DECODE_MULTI_MAX_K, K);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be > 0", fn);
+    if (x == nullptr || w == nullptr || conv_state_in == nullptr || g == nullptr ||
+        beta == nullptr || state_in == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, w, conv_state_in, g, beta and state_in must be non-null", fn);
+    if ((state_out == nullptr) != (conv_state_out == nullptr))
+        return fail(KDA_ERR_INVALID_ARG, "%s: state_out and conv_state_out are given together or not at all", fn);
+    if (o == nullptr && state_out == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: neither o nor the output states are given", fn);
+    if (!aligned16(x) || !aligned16(conv_state_in) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(state_in) || !aligned16(conv_state_out) || !aligned16(state_out) || !aligned16(o))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(n_tokens) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: n_tokens must be 4-byte aligned", fn);
+    if ((int64_t)B * H > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", fn);
+    const int64_t es = esize(dtype);
+    const int64_t P = 3LL * H * D;
+    const int64_t x_b = (int64_t)B * K * P * es, g_b = (int64_t)B * K * H * D * es;
+    const int64_t beta_b = (int64_t)B * K * H * es, o_b = (int64_t)B * K * H * D * es;
+    const int64_t st_b = (int64_t)B * H * D * D * 4, cs_b = (int64_t)B * P * 3 * es;
+    const int64_t nt_b = (int64_t)B * 4;
+    // o overlaps nothing; each output state is its input (in place) or apart
+    // from every other tensor
+    if (overlap(o, o_b, x, x_b) || overlap(o, o_b, conv_state_in, cs_b) || overlap(o, o_b, g, g_b) ||
+        overlap(o, o_b, beta, beta_b) || overlap(o, o_b, state_in, st_b) ||
+        overlap(o, o_b, state_out, st_b) || overlap(o, o_b, conv_state_out, cs_b) ||
+        overlap(o, o_b, n_tokens, nt_b))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not overlap another tensor", fn);
+    if (state_out != nullptr) {
+        if (state_out != state_in && overlap(state_out, st_b, state_in, st_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: state_out partly overlaps state_in", fn);
+        if (conv_state_out != conv_state_in && overlap(conv_state_out, cs_b, conv_state_in, cs_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out partly overlaps conv_state_in", fn);
+        if (overlap(state_out, st_b, x, x_b) || overlap(state_out, st_b, g, g_b) ||
+            overlap(state_out, st_b, beta, beta_b) || overlap(state_out, st_b, conv_state_in, cs_b) ||
+            overlap(state_out, st_b, conv_state_out, cs_b) || overlap(state_out, st_b, n_tokens, nt_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: state_out overlaps another tensor", fn);
+        if (overlap(conv_state_out, cs_b, x, x_b) || overlap(conv_state_out, cs_b, g, g_b) ||
+            overlap(conv_state_out, cs_b, beta, beta_b) || overlap(conv_state_out, cs_b, state_in, st_b) ||
+            overlap(conv_state_out, cs_b, n_tokens, nt_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out overlaps another tensor", fn);
+    }
+    if (B == 0) return ok();
+    return hip_status(kda::launch_decode_multi(x, w, conv_state_in, conv_state_out, g, beta,
+                                               state_in, state_out, o, n_tokens, B, K, H, D,
+                                               dtype, l2_eps, s),
+                      fn);
+}
+
 int kda_gated_norm(const void* o, const void* gate, const float* weight, void* y,
                    int64_t n_tokens, int32_t H, int32_t D, float eps, int32_t dtype,
                    hipStream_t s) {

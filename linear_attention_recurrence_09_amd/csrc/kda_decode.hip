@@ -178,6 +178,201 @@ decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_stat
     }
 }
 
+// Several new tokens per sequence in one pass over the state: the K tokens a
+// drafter proposes are checked in one call ("Kimi K3" on archdiff.com,
+// component list: the MTP layer used as an EAGLE-3 drafter, and speculative
+// decoding by MTP self-drafting).  Each token is the step above; the state of
+// the (sequence, head) and each channel's conv window stay in registers
+// across the tokens, so the state is read once and written at most once per
+// call.  After token n_b of sequence b (n_b = n_tokens[b], clamped to [0, K];
+// K when n_tokens is null) the state and the conv window are stored to
+// state_out / cs_out (when given); outputs are written for all K tokens when
+// o is given, otherwise the loop stops after n_b tokens.
+template <typename T, int D>
+__global__ void __launch_bounds__(kDecThreads)
+decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const T* cs_in,
+                    T* cs_out, const T* __restrict__ g, const T* __restrict__ beta,
+                    const float* state_in, float* state_out, T* __restrict__ o,
+                    const int32_t* __restrict__ n_tokens, int K, int H, float l2_eps) {
+    constexpr int CG = D / 4;                 // float4 column groups per row
+    constexpr int R = kDecThreads / CG;       // row groups
+    constexpr int RPT = D / R;                // rows per thread
+    constexpr int CT = 3 * D / 2;             // conv threads (2 channels each)
+    __shared__ __attribute__((aligned(16))) float su[3 * D];   // token's conv output: q | k | v
+    __shared__ __attribute__((aligned(16))) float sa[D];       // per-key-channel retention
+    __shared__ float sred[kDecThreads / 64][CG][8];
+    __shared__ float skq;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int bh = blockIdx.x;
+    const int b = bh / H;
+    const int h = bh % H;
+    const int P = 3 * H * D;
+    int nb = K;
+    if (n_tokens != nullptr) {
+        nb = n_tokens[b];
+        nb = nb < 0 ? 0 : (nb > K ? K : nb);
+    }
+    const int nt = o != nullptr ? K : nb;
+    const bool snapshot = state_out != nullptr;
+
+    // ---- state loads first: the longest-latency traffic ---------------------
+    // thread (rg, cg) holds rows r0 = rg*RPT .. r0+RPT-1, columns 4cg .. 4cg+3
+    // (32 threads read each 512-byte row), so its k, q and decays are
+    // 16-byte LDS reads
+    static_assert(RPT % 4 == 0, "rows per thread in fours");
+    const int cg = tid % CG;
+    const int rg = tid / CG;
+    const int r0 = rg * RPT;
+    const float* Sin = state_in + (int64_t)bh * D * D;
+    floatx4 sv[RPT];
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+        sv[j] = stream_load(reinterpret_cast<const floatx4*>(Sin + (r0 + j) * D + 4 * cg));
+
+    // ---- this thread's two conv channels: taps and rolling window ----------
+    int part = 3;
+    int64_t c = 0;
+    float wt[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float w0[3] = {0.f, 0.f, 0.f}, w1[3] = {0.f, 0.f, 0.f};   // oldest first
+    if (tid < CT) {
+        const int cc = 2 * tid;               // channel within [q | k | v] of head h
+        part = cc / D;
+        c = (int64_t)part * H * D + h * D + cc % D;
+        const T* sp = cs_in + ((int64_t)b * P + c) * 3;
+        load2(sp, w0[0], w0[1]);
+        load2(sp + 2, w0[2], w1[0]);
+        load2(sp + 4, w1[1], w1[2]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wt[i] = w[c * 4 + i];
+    }
+    auto store_states = [&]() {
+        float* Sout = state_out + (int64_t)bh * D * D;
+#pragma unroll
+        for (int j = 0; j < RPT; ++j)
+            stream_store(sv[j], reinterpret_cast<floatx4*>(Sout + (r0 + j) * D + 4 * cg));
+        if (tid < CT) {
+            T* sp = cs_out + ((int64_t)b * P + c) * 3;
+            store2(sp, w0[0], w0[1]);
+            store2(sp + 2, w0[2], w1[0]);
+            store2(sp + 4, w1[1], w1[2]);
+        }
+    };
+    if (snapshot && nb == 0) store_states();
+
+    for (int t = 0; t < nt; ++t) {
+        const int64_t row = (int64_t)b * K + t;   // token row of x, g, beta and o
+        // the previous token's reads of su, sa, sred and skq are done
+        if (t > 0) __syncthreads();
+
+        // ---- conv window + SiLU + L2 ---------------------------------------
+        float y0 = 0.f, y1 = 0.f;
+        if (tid < CT) {
+            float x0, x1;
+            load2(x + row * P + c, x0, x1);
+            const float p0 = wt[0] * w0[0] + wt[1] * w0[1] + wt[2] * w0[2] + wt[3] * x0;
+            const float p1 = wt[4] * w1[0] + wt[5] * w1[1] + wt[6] * w1[2] + wt[7] * x1;
+            y0 = siluf_(p0);
+            y1 = siluf_(p1);
+            w0[0] = w0[1]; w0[1] = w0[2]; w0[2] = x0;
+            w1[0] = w1[1]; w1[1] = w1[2]; w1[2] = x1;
+        }
+        float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
+        if (part < 2) {
+            const float inv = rsqrt_nr(ss + l2_eps);
+            y0 *= inv;
+            y1 *= inv;
+        }
+        if (tid < CT) {
+            su[2 * tid] = y0;
+            su[2 * tid + 1] = y1;
+        }
+        if (tid < D) sa[tid] = fast_exp2(clamp_log_decay(to_f(g[(row * H + h) * D + tid])) * kLog2e);
+        const float bt = to_f(beta[row * H + h]);
+        __syncthreads();
+
+        if (wave == 0) {   // k . q
+            float kq = 0.f;
+            for (int i = lane; i < D; i += 64) kq += su[i] * su[D + i];
+            kq = group_sum<64>(kq);
+            if (lane == 0) skq = kq;
+        }
+
+        // ---- decay, and the column sums Sbar^T k, Sbar^T q ------------------
+        float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
+        floatx4 kr[RPT / 4];   // k of this thread's rows, kept for the write
+#pragma unroll
+        for (int j4 = 0; j4 < RPT / 4; ++j4) {
+            const floatx4 a4 = *reinterpret_cast<const floatx4*>(sa + r0 + 4 * j4);
+            const floatx4 q4 = *reinterpret_cast<const floatx4*>(su + r0 + 4 * j4);
+            kr[j4] = *reinterpret_cast<const floatx4*>(su + D + r0 + 4 * j4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * j4 + e;
+                sv[j] *= a4[e];
+                const float ki = kr[j4][e], qi = q4[e];
+                ak.x += ki * sv[j][0]; ak.y += ki * sv[j][1]; ak.z += ki * sv[j][2]; ak.w += ki * sv[j][3];
+                aq.x += qi * sv[j][0]; aq.y += qi * sv[j][1]; aq.z += qi * sv[j][2]; aq.w += qi * sv[j][3];
+            }
+        }
+#pragma unroll
+        for (int m = CG; m < 64; m <<= 1) {
+            ak.x += __shfl_xor(ak.x, m, 64); ak.y += __shfl_xor(ak.y, m, 64);
+            ak.z += __shfl_xor(ak.z, m, 64); ak.w += __shfl_xor(ak.w, m, 64);
+            aq.x += __shfl_xor(aq.x, m, 64); aq.y += __shfl_xor(aq.y, m, 64);
+            aq.z += __shfl_xor(aq.z, m, 64); aq.w += __shfl_xor(aq.w, m, 64);
+        }
+        if (lane < CG) {
+            float* r = sred[wave][cg];
+            r[0] = ak.x; r[1] = ak.y; r[2] = ak.z; r[3] = ak.w;
+            r[4] = aq.x; r[5] = aq.y; r[6] = aq.z; r[7] = aq.w;
+        }
+        __syncthreads();
+        float tk[4] = {0.f, 0.f, 0.f, 0.f}, tq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wv = 0; wv < kDecThreads / 64; ++wv)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tk[e] += sred[wv][cg][e];
+                tq[e] += sred[wv][cg][4 + e];
+            }
+        const float kq = skq;
+        float ev[4], ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ev[e] = su[2 * D + 4 * cg + e] - tk[e];
+            ov[e] = tq[e] + bt * kq * ev[e];
+        }
+        if (o != nullptr && rg == 0) {
+            T* op = o + (row * H + h) * D + 4 * cg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) op[e] = from_f<T>(ov[e]);
+        }
+        // ---- write: S = Sbar + beta k e^T -----------------------------------
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const float bk = bt * kr[j / 4][j % 4];
+            sv[j][0] += bk * ev[0]; sv[j][1] += bk * ev[1]; sv[j][2] += bk * ev[2]; sv[j][3] += bk * ev[3];
+        }
+        if (snapshot && t == nb - 1) store_states();
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_decode_multi_t(const void* x, const float* w, const void* cs_in, void* cs_out,
+                                 const void* g, const void* beta, const float* state_in,
+                                 float* state_out, void* o, const int32_t* n_tokens, int B, int K,
+                                 int H, float l2_eps, hipStream_t s) {
+    const int64_t blocks = (int64_t)B * H;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_multi_kernel<T, D>), dim3((unsigned)blocks), dim3(kDecThreads), 0,
+                       s, (const T*)x, w, (const T*)cs_in, (T*)cs_out, (const T*)g,
+                       (const T*)beta, state_in, state_out, (T*)o, n_tokens, K, H, l2_eps);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_decode_t(const void* x, const float* w, void* conv_state, const void* g,
                            const void* beta, float* state, void* o, int B, int H, float l2_eps,
@@ -205,6 +400,22 @@ hipError_t launch_decode(const void* x, const float* w, void* conv_state, const 
                                                  l2_eps, s)
                    : launch_decode_t<__bf16, 128>(x, w, conv_state, g, beta, state, o, B, H,
                                                   l2_eps, s);
+}
+
+hipError_t launch_decode_multi(const void* x, const float* w, const void* cs_in, void* cs_out,
+                               const void* g, const void* beta, const float* state_in,
+                               float* state_out, void* o, const int32_t* n_tokens, int B, int K,
+                               int H, int D, int dtype, float l2_eps, hipStream_t s) {
+    if (dtype == 0) {
+        return D == 64 ? launch_decode_multi_t<float, 64>(x, w, cs_in, cs_out, g, beta, state_in,
+                                                          state_out, o, n_tokens, B, K, H, l2_eps, s)
+                       : launch_decode_multi_t<float, 128>(x, w, cs_in, cs_out, g, beta, state_in,
+                                                           state_out, o, n_tokens, B, K, H, l2_eps, s);
+    }
+    return D == 64 ? launch_decode_multi_t<__bf16, 64>(x, w, cs_in, cs_out, g, beta, state_in,
+                                                       state_out, o, n_tokens, B, K, H, l2_eps, s)
+                   : launch_decode_multi_t<__bf16, 128>(x, w, cs_in, cs_out, g, beta, state_in,
+                                                        state_out, o, n_tokens, B, K, H, l2_eps, s);
 }
 
 }  // namespace kda

@@ -18,6 +18,13 @@ hipError_t launch_decode(const void* x, const float* w, void* conv_state, const 
                          const void* beta, float* state, void* o, int B, int H, int D,
                          int dtype, float l2_eps, hipStream_t s);
 
+// K tokens per sequence from state_in / cs_in; states after n_tokens[b]
+// tokens to state_out / cs_out (both null: outputs only).
+hipError_t launch_decode_multi(const void* x, const float* w, const void* cs_in, void* cs_out,
+                               const void* g, const void* beta, const float* state_in,
+                               float* state_out, void* o, const int32_t* n_tokens, int B, int K,
+                               int H, int D, int dtype, float l2_eps, hipStream_t s);
+
 // Chunked prefill configuration chosen on the host.
 struct ChunkPlan {
     int nb;       // 16-token blocks per chunk (chunk = 16 * nb)

@@ -28,9 +28,9 @@ def L():
     return kda.lib()
 
 
-def test_header_declares_the_four_calls():
-    assert declared() == ["kda_chunk_prefill", "kda_conv", "kda_decode_step", "kda_gated_norm",
-                          "kda_last_error", "kda_version"]
+def test_header_declares_the_calls():
+    assert declared() == ["kda_chunk_prefill", "kda_conv", "kda_decode_multi", "kda_decode_step",
+                          "kda_gated_norm", "kda_last_error", "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -100,3 +100,30 @@ def test_decode_and_norm_argument_checks(L):
     assert norm(o=None) == INVALID
     assert norm(y=A + 8 * MB) == INVALID                     # y overlaps gate
     assert norm(y=A + 16) == INVALID                         # partial overlap with o
+
+
+def test_decode_multi_argument_checks(L):
+    # B=4, K=3, H=2, D=128, bf16: every tensor below 1 MB, placed 1 MB apart
+    def dm(x=A, cs_in=A + MB, cs_out=A + 2 * MB, g=A + 3 * MB, b=A + 4 * MB, st_in=A + 5 * MB,
+           st_out=A + 6 * MB, o=A + 7 * MB, n=None, B=4, K=3, D=128, eps=1e-6):
+        return L.kda_decode_multi(x, A + 8 * MB, cs_in, cs_out, g, b, st_in, st_out, o, n, B, K,
+                                  2, D, 1, eps, None)
+    assert dm(x=None) == INVALID
+    assert dm(st_in=None) == INVALID
+    assert dm(K=0) == INVALID
+    assert dm(K=65) == UNSUPPORTED
+    assert dm(D=32) == UNSUPPORTED
+    assert dm(eps=0.0) == INVALID
+    assert dm(st_out=None) == INVALID                        # states come in pairs
+    assert dm(o=None, st_out=None, cs_out=None) == INVALID   # nothing to compute
+    assert dm(o=A + 16) == INVALID                           # o overlaps x
+    assert dm(o=A + 6 * MB) == INVALID                       # o overlaps state_out
+    assert dm(st_out=A + 5 * MB + 16) == INVALID             # partial overlap with state_in
+    assert dm(cs_out=A + MB + 64) == INVALID                 # partial overlap with conv_state_in
+    assert dm(st_out=A + 3 * MB) == INVALID                  # state_out over g
+    assert dm(n=A + 9 * MB + 2) == INVALID                   # misaligned n_tokens
+    assert dm(x=A + 8) == INVALID                            # misaligned x
+    assert "kda_decode_multi" in kda.kda_last_error()
+    assert dm(B=0) == OK
+    assert dm(B=0, st_out=A + 5 * MB, cs_out=A + MB) == OK   # in place passes the checks
+    assert dm(B=0, st_out=None, cs_out=None) == OK           # outputs only
