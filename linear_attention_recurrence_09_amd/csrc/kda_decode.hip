@@ -1,4 +1,5 @@
-// kda_decode.hip -- one decode step of the KDA mixer for B sequences (gfx950).
+// kda_decode.hip -- decode steps of the KDA mixer (gfx950): one new token,
+// or K drafted tokens, for each of B sequences.
 //
 // "Inside Kimi K3" (lei.chat), KDA short-convolution diagram: autoregressive
 // decoding keeps the 3 previous raw inputs of every channel of the combined
@@ -9,11 +10,11 @@
 //
 // One workgroup per (sequence, head).  The state is one streaming pass: each
 // of 256 threads loads its 16 (D = 128) float4 of S (non-temporal: the state
-// is streamed once per step), decays them, accumulates
+// is streamed once per call), and per token decays them, accumulates
 // Sbar^T k and Sbar^T q for its 4 columns, the column sums are reduced across
-// row groups, and the same registers are updated and stored.  The read uses
+// row groups, and the same registers take the rank-1 write.  The read uses
 // o = Sbar^T q + beta (k . q) e, which equals S_t^T q.  HBM traffic is one read
-// and one write of the fp32 state plus the small per-token tensors.
+// and at most one write of the fp32 state plus the small per-token tensors.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -46,138 +47,6 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 #endif
 }
 
-template <typename T, int D>
-__global__ void __launch_bounds__(kDecThreads)
-decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_state,
-              const T* __restrict__ g, const T* __restrict__ beta, float* state,
-              T* __restrict__ o, int H, float l2_eps) {
-    constexpr int CG = D / 4;                 // float4 column groups per row
-    constexpr int R = kDecThreads / CG;       // row groups
-    constexpr int RPT = D / R;                // rows per thread
-    constexpr int CT = 3 * D / 2;             // conv threads (2 channels each)
-    __shared__ float su[3 * D];               // conv output: q | k | v of this head
-    __shared__ float sa[D];                   // per-key-channel retention
-    __shared__ float sred[kDecThreads / 64][CG][8];
-    __shared__ float skq;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int bh = blockIdx.x;
-    const int b = bh / H;
-    const int h = bh % H;
-    const int P = 3 * H * D;
-
-    // ---- state loads first: the longest-latency traffic ---------------------
-    const int cg = tid % CG;
-    const int rg = tid / CG;
-    float* Sbh = state + (int64_t)bh * D * D;
-    floatx4 sv[RPT];   // streamed once: non-temporal loads and stores
-#pragma unroll
-    for (int j = 0; j < RPT; ++j)
-        sv[j] = stream_load(reinterpret_cast<const floatx4*>(Sbh + (rg + R * j) * D + 4 * cg));
-
-    // ---- conv window + SiLU + L2 -------------------------------------------
-    float y0 = 0.f, y1 = 0.f;
-    int part = 3;
-    if (tid < CT) {
-        const int cc = 2 * tid;               // channel within [q | k | v] of head h
-        part = cc / D;
-        const int d = cc % D;
-        const int c = part * H * D + h * D + d;
-        float x0, x1;
-        load2(x + (int64_t)b * P + c, x0, x1);
-        T* sp = conv_state + ((int64_t)b * P + c) * 3;
-        float s00, s01, s02, s10, s11, s12;
-        load2(sp, s00, s01);
-        load2(sp + 2, s02, s10);
-        load2(sp + 4, s11, s12);
-        const float* wc = w + c * 4;
-        const float p0 = wc[0] * s00 + wc[1] * s01 + wc[2] * s02 + wc[3] * x0;
-        const float p1 = wc[4] * s10 + wc[5] * s11 + wc[6] * s12 + wc[7] * x1;
-        y0 = siluf_(p0);
-        y1 = siluf_(p1);
-        store2(sp, s01, s02);
-        store2(sp + 2, x0, s11);
-        store2(sp + 4, s12, x1);
-    }
-    float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
-    if (part < 2) {
-        const float inv = rsqrt_nr(ss + l2_eps);
-        y0 *= inv;
-        y1 *= inv;
-    }
-    if (tid < CT) {
-        su[2 * tid] = y0;
-        su[2 * tid + 1] = y1;
-    }
-    if (tid < D) sa[tid] = fast_exp2(clamp_log_decay(to_f(g[(int64_t)bh * D + tid])) * kLog2e);
-    const float bt = to_f(beta[bh]);
-    __syncthreads();
-
-    if (wave == 0) {   // k . q
-        float kq = 0.f;
-        for (int i = lane; i < D; i += 64) kq += su[i] * su[D + i];
-        kq = group_sum<64>(kq);
-        if (lane == 0) skq = kq;
-    }
-
-    // ---- decay, and the column sums Sbar^T k, Sbar^T q ----------------------
-    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int i = rg + R * j;
-        const float a = sa[i];
-        sv[j] *= a;
-        const float ki = su[D + i], qi = su[i];
-        ak.x += ki * sv[j][0]; ak.y += ki * sv[j][1]; ak.z += ki * sv[j][2]; ak.w += ki * sv[j][3];
-        aq.x += qi * sv[j][0]; aq.y += qi * sv[j][1]; aq.z += qi * sv[j][2]; aq.w += qi * sv[j][3];
-    }
-    // row groups inside a wave differ in lane bits >= log2(CG)
-#pragma unroll
-    for (int m = CG; m < 64; m <<= 1) {
-        ak.x += __shfl_xor(ak.x, m, 64); ak.y += __shfl_xor(ak.y, m, 64);
-        ak.z += __shfl_xor(ak.z, m, 64); ak.w += __shfl_xor(ak.w, m, 64);
-        aq.x += __shfl_xor(aq.x, m, 64); aq.y += __shfl_xor(aq.y, m, 64);
-        aq.z += __shfl_xor(aq.z, m, 64); aq.w += __shfl_xor(aq.w, m, 64);
-    }
-    if (lane < CG) {
-        float* r = sred[wave][cg];
-        r[0] = ak.x; r[1] = ak.y; r[2] = ak.z; r[3] = ak.w;
-        r[4] = aq.x; r[5] = aq.y; r[6] = aq.z; r[7] = aq.w;
-    }
-    __syncthreads();
-    float tk[4] = {0.f, 0.f, 0.f, 0.f}, tq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int wv = 0; wv < kDecThreads / 64; ++wv)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            tk[e] += sred[wv][cg][e];
-            tq[e] += sred[wv][cg][4 + e];
-        }
-    const float kq = skq;
-    float ev[4], ov[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        ev[e] = su[2 * D + 4 * cg + e] - tk[e];
-        ov[e] = tq[e] + bt * kq * ev[e];
-    }
-    if (rg == 0) {
-        T* op = o + (int64_t)bh * D + 4 * cg;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) op[e] = from_f<T>(ov[e]);
-    }
-    // ---- write: S = Sbar + beta k e^T ---------------------------------------
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-        const int i = rg + R * j;
-        const float bk = bt * su[D + i];
-        floatx4 r = sv[j];
-        r[0] += bk * ev[0]; r[1] += bk * ev[1]; r[2] += bk * ev[2]; r[3] += bk * ev[3];
-        stream_store(r, reinterpret_cast<floatx4*>(Sbh + i * D + 4 * cg));
-    }
-}
-
 // Several new tokens per sequence in one pass over the state: the K tokens a
 // drafter proposes are checked in one call ("Kimi K3" on archdiff.com,
 // component list: the MTP layer used as an EAGLE-3 drafter, and speculative
@@ -188,7 +57,15 @@ decode_kernel(const T* __restrict__ x, const float* __restrict__ w, T* conv_stat
 // K when n_tokens is null) the state and the conv window are stored to
 // state_out / cs_out (when given); outputs are written for all K tokens when
 // o is given, otherwise the loop stops after n_b tokens.
-template <typename T, int D>
+//
+// Two layouts of the state in registers (kStrided): thread (rg, cg) holds
+// columns 4cg .. 4cg+3 of rows rg + R j (each load instruction covers R
+// adjacent rows; the q, k and decay of key channel i then sit in LDS at
+// position (i % R) RPT + i / R) or of rows rg RPT + j (consecutive; fewer
+// registers).  Either way a thread's q, k and decays are 16-byte LDS reads.
+// The strided layout streams faster; the consecutive one keeps three
+// workgroups per CU, which pays once several tokens' arithmetic dominates.
+template <typename T, int D, bool kStrided>
 __global__ void __launch_bounds__(kDecThreads)
 decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const T* cs_in,
                     T* cs_out, const T* __restrict__ g, const T* __restrict__ beta,
@@ -219,18 +96,17 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
     const bool snapshot = state_out != nullptr;
 
     // ---- state loads first: the longest-latency traffic ---------------------
-    // thread (rg, cg) holds rows r0 = rg*RPT .. r0+RPT-1, columns 4cg .. 4cg+3
-    // (32 threads read each 512-byte row), so its k, q and decays are
-    // 16-byte LDS reads
     static_assert(RPT % 4 == 0, "rows per thread in fours");
     const int cg = tid % CG;
     const int rg = tid / CG;
-    const int r0 = rg * RPT;
+    const int r0 = rg * RPT;   // LDS position of this thread's first row
+    auto srow = [&](int j) { return kStrided ? rg + R * j : r0 + j; };   // state row
+    auto pos = [](int i) { return kStrided ? (i % R) * RPT + i / R : i; };   // LDS position
     const float* Sin = state_in + (int64_t)bh * D * D;
     floatx4 sv[RPT];
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
-        sv[j] = stream_load(reinterpret_cast<const floatx4*>(Sin + (r0 + j) * D + 4 * cg));
+        sv[j] = stream_load(reinterpret_cast<const floatx4*>(Sin + srow(j) * D + 4 * cg));
 
     // ---- this thread's two conv channels: taps and rolling window ----------
     int part = 3;
@@ -252,7 +128,7 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
         float* Sout = state_out + (int64_t)bh * D * D;
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
-            stream_store(sv[j], reinterpret_cast<floatx4*>(Sout + (r0 + j) * D + 4 * cg));
+            stream_store(sv[j], reinterpret_cast<floatx4*>(Sout + srow(j) * D + 4 * cg));
         if (tid < CT) {
             T* sp = cs_out + ((int64_t)b * P + c) * 3;
             store2(sp, w0[0], w0[1]);
@@ -286,10 +162,11 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
             y1 *= inv;
         }
         if (tid < CT) {
-            su[2 * tid] = y0;
-            su[2 * tid + 1] = y1;
+            const int cc = 2 * tid - part * D;   // channel within q, k or v
+            su[part * D + (part < 2 ? pos(cc) : cc)] = y0;
+            su[part * D + (part < 2 ? pos(cc + 1) : cc + 1)] = y1;
         }
-        if (tid < D) sa[tid] = fast_exp2(clamp_log_decay(to_f(g[(row * H + h) * D + tid])) * kLog2e);
+        if (tid < D) sa[pos(tid)] = fast_exp2(clamp_log_decay(to_f(g[(row * H + h) * D + tid])) * kLog2e);
         const float bt = to_f(beta[row * H + h]);
         __syncthreads();
 
@@ -367,40 +244,21 @@ hipError_t launch_decode_multi_t(const void* x, const float* w, const void* cs_i
                                  int H, float l2_eps, hipStream_t s) {
     const int64_t blocks = (int64_t)B * H;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_multi_kernel<T, D>), dim3((unsigned)blocks), dim3(kDecThreads), 0,
-                       s, (const T*)x, w, (const T*)cs_in, (T*)cs_out, (const T*)g,
-                       (const T*)beta, state_in, state_out, (T*)o, n_tokens, K, H, l2_eps);
-    return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t launch_decode_t(const void* x, const float* w, void* conv_state, const void* g,
-                           const void* beta, float* state, void* o, int B, int H, float l2_eps,
-                           hipStream_t s) {
-    const int64_t blocks = (int64_t)B * H;
-    if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, D>), dim3((unsigned)blocks), dim3(kDecThreads), 0, s,
-                       (const T*)x, w, (T*)conv_state, (const T*)g, (const T*)beta, state, (T*)o,
-                       H, l2_eps);
+    // up to two tokens the state streaming dominates: strided rows
+    if (K <= 2)
+        hipLaunchKernelGGL((decode_multi_kernel<T, D, true>), dim3((unsigned)blocks),
+                           dim3(kDecThreads), 0, s, (const T*)x, w, (const T*)cs_in, (T*)cs_out,
+                           (const T*)g, (const T*)beta, state_in, state_out, (T*)o, n_tokens, K,
+                           H, l2_eps);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<T, D, false>), dim3((unsigned)blocks),
+                           dim3(kDecThreads), 0, s, (const T*)x, w, (const T*)cs_in, (T*)cs_out,
+                           (const T*)g, (const T*)beta, state_in, state_out, (T*)o, n_tokens, K,
+                           H, l2_eps);
     return hipGetLastError();
 }
 
 }  // namespace
-
-hipError_t launch_decode(const void* x, const float* w, void* conv_state, const void* g,
-                         const void* beta, float* state, void* o, int B, int H, int D,
-                         int dtype, float l2_eps, hipStream_t s) {
-    if (dtype == 0) {
-        return D == 64 ? launch_decode_t<float, 64>(x, w, conv_state, g, beta, state, o, B, H,
-                                                    l2_eps, s)
-                       : launch_decode_t<float, 128>(x, w, conv_state, g, beta, state, o, B, H,
-                                                     l2_eps, s);
-    }
-    return D == 64 ? launch_decode_t<__bf16, 64>(x, w, conv_state, g, beta, state, o, B, H,
-                                                 l2_eps, s)
-                   : launch_decode_t<__bf16, 128>(x, w, conv_state, g, beta, state, o, B, H,
-                                                  l2_eps, s);
-}
 
 hipError_t launch_decode_multi(const void* x, const float* w, const void* cs_in, void* cs_out,
                                const void* g, const void* beta, const float* state_in,
@@ -416,6 +274,14 @@ hipError_t launch_decode_multi(const void* x, const float* w, const void* cs_in,
                                                        state_out, o, n_tokens, B, K, H, l2_eps, s)
                    : launch_decode_multi_t<__bf16, 128>(x, w, cs_in, cs_out, g, beta, state_in,
                                                         state_out, o, n_tokens, B, K, H, l2_eps, s);
+}
+
+// One token: the states are updated in place.
+hipError_t launch_decode(const void* x, const float* w, void* conv_state, const void* g,
+                         const void* beta, float* state, void* o, int B, int H, int D,
+                         int dtype, float l2_eps, hipStream_t s) {
+    return launch_decode_multi(x, w, conv_state, conv_state, g, beta, state, state, o, nullptr, B,
+                               1, H, D, dtype, l2_eps, s);
 }
 
 }  // namespace kda
