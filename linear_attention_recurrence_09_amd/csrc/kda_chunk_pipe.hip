@@ -23,11 +23,13 @@
 //  * Producer waves (8, two per SIMD) build everything that does not depend
 //    on the state, one whole chunk per wave: per-channel decay products with
 //    each lane holding all 16 tokens of its channels, the operand tiles -Kt,
-//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  The 16 x 16
-//    unit triangular inverses are done in batches of two chunks: the producer
-//    that finishes a batch last solves both by back substitution in
-//    registers, one chunk per pair of 16-lane rows (row broadcasts by DPP).
-//    Results go to a ring of LDS slots.
+//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  Each 16 x 16
+//    unit triangular inverse is solved by back substitution in registers
+//    (row broadcasts by DPP) by the chunk's own producer, so a chunk never
+//    waits for another producer.  (Batches of two or four chunks, solved by
+//    the batch's last producer on separate 16-lane rows, spend less VALU but
+//    couple the producers' latencies; they stay selectable.)  Results go to
+//    a ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
 //    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
@@ -97,9 +99,9 @@ constexpr int kRing = 8;               // LDS slots
 #define KDA_PIPE_EARLY 0                // producers do the decay arithmetic before taking the slot
 #endif
 #ifndef KDA_PIPE_BATCH
-#define KDA_PIPE_BATCH 2
+#define KDA_PIPE_BATCH 1
 #endif
-constexpr int kBatch = KDA_PIPE_BATCH;  // chunks per triangular-inverse batch (2 or 4)
+constexpr int kBatch = KDA_PIPE_BATCH;  // chunks per triangular-inverse batch (1, 2 or 4)
 constexpr int kNBatch = kRing / kBatch; // batches in flight
 constexpr int kSpinLimit = 1 << 17;    // polls (about 128 cycles each) before giving up
 #ifndef KDA_PIPE_SLEEP
@@ -144,7 +146,8 @@ struct PipeCfg {
     // every producer keeps one slot (rings whose size does not divide the
     // producer count gave wrong results in tests)
     static_assert(kNP % kRing == 0, "ring size divides the producer count");
-    static_assert((kBatch == 2 || kBatch == 4) && kRing % kBatch == 0, "inverse batches cover the ring");
+    static_assert((kBatch == 1 || kBatch == 2 || kBatch == 4) && kRing % kBatch == 0,
+                  "inverse batches cover the ring");
 };
 
 // Position of channel c inside its 32-channel group in the permuted tiles:
@@ -537,10 +540,11 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk, in batches ------------
             // This chunk's part: column c = lr of -N holds -beta_c A_kk[c][r]
             // for r < c; lane (q, c) has rows r = 4q+i (the tile holds -Kt, so
-            // akk[i] = -A_kk[c][4q+i]).  It waits in LDS, with beta, until the
-            // last chunk of its batch to get here inverts the whole batch, one
-            // chunk per 4/kBatch of the 16-lane rows (the row broadcasts of the
-            // back substitution stay inside a row), so fewer rows repeat work.
+            // akk[i] = -A_kk[c][4q+i]).  It goes through LDS, with beta (to the
+            // column layout of the solve), and the last chunk of its batch to
+            // get here inverts the whole batch -- with one chunk per batch, this
+            // wave, right away -- one chunk per 4/kBatch of the 16-lane rows
+            // (the row broadcasts of the back substitution stay inside a row).
             constexpr int RPC = 4 / kBatch;   // lane rows per chunk
             const int cix = (int)ci;
             const int bt = cix / kBatch, bslot = bt % kNBatch;
