@@ -146,8 +146,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--counters", action="store_true",
-                    help="short run for rocprofv3 counter passes: a few chunk-kernel launches "
-                         "at T=65536 plus a plain copy kernel of known size for calibration")
+                    help="short run for rocprofv3 counter passes: each kernel a few times "
+                         "(conv, chunk, norm at T=65536; decode at B=256) plus a plain copy "
+                         "kernel of known size for calibration")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA mixer here is a single-GPU library "
@@ -201,12 +202,30 @@ def main():
             kda.kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD,
                                   g, beta, o, 1, N, H, D, D, chunk=C, final_state=sT,
                                   stream=stream)
+        kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
+        # the decode kernels: three one-token steps, two calls of four tokens
+        dspec = synth.CONFIGS[4]
+        Bd, Hd, Dd = dspec.B, dspec.H, dspec.D
+        d = synth.decode_inputs(dspec, device="cuda", steps=4)
+        od = torch.empty((Bd, Hd, Dd), dtype=d["x"].dtype, device="cuda")
+        cs, S = d["conv_state"].clone(), d["S0"].clone()
+        for t in range(3):
+            kda.kda_decode_step(d["x"][t], d["conv_w"], cs, d["g"][t], d["beta"][t], S, od, Bd,
+                                Hd, Dd, stream=stream)
+        xb, gb, bb = (d[n].transpose(0, 1).contiguous() for n in ("x", "g", "beta"))
+        om = torch.empty((Bd, 4, Hd, Dd), dtype=d["x"].dtype, device="cuda")
+        for _ in range(2):
+            kda.kda_decode_multi(xb, d["conv_w"], cs, gb, bb, S, Bd, 4, Hd, Dd, o=om,
+                                 conv_state_out=cs, state_out=S, stream=stream)
+        torch.cuda.synchronize()
+        del d, cs, S, xb, gb, bb, om
         src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("counter run done: 3 chunk launches, 3 copies of 2 GiB")
+        log("counter run done: conv, 3 chunk launches, norm, 3 decode steps, 2 four-token "
+            "decode calls, 3 copies of 2 GiB")
         return
 
     for _ in range(args.warmup):

@@ -11,8 +11,9 @@ Inputs (CSV files written by the commands recorded in the summaries):
   --write  <dir>/write_counter_collection.csv from
            rocprofv3 --pmc WRITE_SIZE -T -f csv -d <dir> -o write -- python3 bench.py --counters
 
-Writes profiles/chunk_prefill_T65536_kernel_stats.txt and
-profiles/chunk_prefill_T65536_traffic.json.  The byte counters (KiB per
+Writes profiles/chunk_prefill_T65536_kernel_stats.txt,
+profiles/chunk_prefill_T65536_traffic.json and, for every kernel of the
+counter run, profiles/kernels_traffic_T65536_B256.txt.  The byte counters (KiB per
 dispatch) are scaled by what the same counter reads for bench.py's copy
 kernel of known size (2 GiB read, 2 GiB written); the JSON records the hash
 of the chunk-kernel sources so bench.py can tell whether it is current.
@@ -115,7 +116,38 @@ def main():
               f"#   WRITE_SIZE {rec['write_kib_per_dispatch']:.0f} KiB x {w_scale:.3f} = {wb/1e9:.3f} GB",
               f"#   traffic {(fb+wb)/1e9:.3f} GB vs algorithmic {algo/1e9:.3f} GB "
               f"({rec['traffic_over_algorithmic']:.3f}x)"]
+    # every kernel of the counter run against its algorithmic bytes
+    pb = bench.prefill_bytes(65536, 96, 128, 1)
+    kinds = [
+        ("conv (kda_conv, T=65536)", "conv_kernel", pb["conv"]),
+        ("chunk (kda_chunk_prefill, chunk 16, T=65536)", CHUNK_TAG, pb["chunk"]),
+        ("gated norm (kda_gated_norm, T=65536)", "gated_norm_kernel", pb["norm"]),
+        ("decode, 1 token (kda_decode_step, B=256)", "decode_multi_kernelIDF16bLi128ELb1",
+         bench.decode_bytes(256, 96, 128)),
+        ("decode, 4 tokens (kda_decode_multi, B=256)", "decode_multi_kernelIDF16bLi128ELb0",
+         bench.decode_multi_bytes(256, 4, 96, 128)),
+    ]
+    table = ["# HBM bytes per dispatch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two runs of",
+             "#   python3 bench.py --counters), scaled by the same counters on a copy kernel",
+             f"#   of 2 GiB in / 2 GiB out (fetch x{f_scale:.3f}, write x{w_scale:.3f}), MI355X",
+             "# commands: rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters",
+             "#           rocprofv3 --pmc WRITE_SIZE -T -f csv -d <dir> -o write -- python3 bench.py --counters",
+             f"{'kernel':46s} {'n':>2s} {'fetch_GB':>9s} {'write_GB':>9s} {'traffic_GB':>10s} "
+             f"{'algo_GB':>9s} {'ratio':>6s}"]
+    for label, tag, algo_b in kinds:
+        fk = [v for n, v in fetch if tag in n]
+        wk = [v for n, v in write if tag in n]
+        if not fk or not wk:
+            table.append(f"{label:46s}  no dispatches")
+            continue
+        fbk = statistics.mean(fk) * 1024 * f_scale
+        wbk = statistics.mean(wk) * 1024 * w_scale
+        table.append(f"{label:46s} {len(fk):2d} {fbk/1e9:9.3f} {wbk/1e9:9.3f} {(fbk+wbk)/1e9:10.3f} "
+                     f"{algo_b/1e9:9.3f} {(fbk+wbk)/algo_b:6.3f}")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "kernels_traffic_T65536_B256.txt"), "w") as f:
+        f.write("\n".join(table) + "\n")
+    print("\n".join(table))
     with open(os.path.join(ROOT, "profiles", "chunk_prefill_T65536_kernel_stats.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(bench.TRAFFIC_FILE, "w") as f:
