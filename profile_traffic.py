@@ -45,13 +45,71 @@ def per_dispatch(path, counter):
     return [(names[d], vals[d]) for d in sorted(vals, key=int)]
 
 
+PMC_PASSES = [
+    "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INST_CYCLES_SALU GRBM_GUI_ACTIVE",
+    "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES "
+    "SQ_ACTIVE_INST_LDS SQ_INSTS_VMEM SQ_ACTIVE_INST_SCA GRBM_GUI_ACTIVE",
+]
+
+
+def counters_by_dispatch(path):
+    """{dispatch: (kernel name, {counter: value summed over SEs and XCCs})}."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        name, vals = out.setdefault(d, (r["Kernel_Name"], {}))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def pmc_summary(pmc1, pmc2, n_xcc=8, cu_active=192, simd_per_cu=4, chunks=4096):
+    """Busy fractions and instruction mix of the chunk kernel from two
+    counter passes (derived the way rocprofv3's VALUBusy, SALUBusy, MfmaUtil
+    and LdsUtil are, over the CUs the kernel occupies)."""
+    rows = {}
+    for path in (pmc1, pmc2):
+        for d, (name, vals) in counters_by_dispatch(path).items():
+            if CHUNK_TAG in name:
+                rows.setdefault(d, {}).update(vals)
+    last = [rows[d] for d in sorted(rows)][-1]
+    cycles = last["GRBM_GUI_ACTIVE"] / n_xcc          # per XCC
+    per_chunk = lambda c: last[c] / cu_active / chunks
+    lines = ["# rocprofv3 counters of the chunk kernel (chunk 16, T=65536, H=96, D=128, bf16), MI355X,",
+             "# last of its three dispatches in `python3 bench.py --counters`; two passes:"]
+    lines += [f"#   rocprofv3 --pmc {p} -T -f csv -d <dir> -o pmcN -- python3 bench.py --counters"
+              for p in PMC_PASSES]
+    lines += [f"# {cu_active} CUs active (one workgroup each), {chunks} chunks per workgroup, "
+              f"{cycles:.3g} shader cycles per XCC", ""]
+    lines.append(f"VALU busy  {100 * last['SQ_ACTIVE_INST_VALU'] / cu_active / cycles:5.1f} % "
+                 "(SQ_ACTIVE_INST_VALU over the active CUs)")
+    lines.append(f"SALU busy  {100 * last['SQ_INST_CYCLES_SALU'] / cu_active / cycles:5.1f} %")
+    lines.append(f"MFMA busy  {100 * last['SQ_VALU_MFMA_BUSY_CYCLES'] / (cu_active * simd_per_cu) / cycles:5.1f} % "
+                 "(SQ_VALU_MFMA_BUSY_CYCLES over the active SIMDs)")
+    lines.append(f"LDS busy   {100 * last['SQ_LDS_IDX_ACTIVE'] / cu_active / cycles:5.1f} %, of which bank "
+                 f"conflicts {100 * last['SQ_LDS_BANK_CONFLICT'] / last['SQ_LDS_IDX_ACTIVE']:4.1f} %")
+    lines.append("instructions per chunk per CU: " + ", ".join(
+        f"{k[9:].lower()} {per_chunk(k):.0f}" for k in
+        ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM")))
+    lines.append(f"shader cycles per chunk: {cycles / chunks:.0f}")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
+    ap.add_argument("--pmc1", help="counter_collection.csv of the first counter pass (optional)")
+    ap.add_argument("--pmc2", help="counter_collection.csv of the second counter pass")
     args = ap.parse_args()
     import bench
+    if args.pmc1 and args.pmc2:
+        pl = pmc_summary(args.pmc1, args.pmc2)
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        with open(os.path.join(ROOT, "profiles", "chunk_prefill_T65536_pmc.txt"), "w") as f:
+            f.write("\n".join(pl) + "\n")
+        print("\n".join(pl))
 
     # kernel-trace statistics
     rows = list(csv.DictReader(open(args.trace)))
