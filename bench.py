@@ -278,6 +278,53 @@ def main():
         "pipeline_gbs": sum(nbytes.values()) / (ms_step * 1e-3) / 1e9,
     }
 
+    # the other two prefill workloads, timed the same way (informative: the
+    # headline value is the workload above)
+    extra = {}
+    for cid in (1, 3):
+        es = synth.CONFIGS[cid]
+        ei = synth.prefill_inputs(es, device="cuda")
+        Ne, Se = ei["x"].shape[0], len(ei["lengths"])
+        cu = (torch.tensor(ei["cu"], dtype=torch.int32, device="cuda") if es.varlen else None)
+        ye = torch.empty_like(ei["x"])
+        oe = torch.empty((Ne, H, D), dtype=ei["x"].dtype, device="cuda")
+        yn = torch.empty_like(oe)
+        sTe = torch.empty((Se, H, D, D), dtype=torch.float32, device="cuda")
+        Be, Te = (1, Ne) if es.varlen else (Se, Ne // Se)
+
+        def estep(events=None):
+            if events:
+                events[0].record(stream)
+            kda.kda_conv(ei["x"], ei["conv_w"], ye, Be, Te, H, D, cu_seqlens=cu, num_seqs=Se,
+                         stream=stream)
+            if events:
+                events[1].record(stream)
+            kda.kda_chunk_prefill(ye[:, :HD], ye[:, HD:2 * HD], ye[:, 2 * HD:], 3 * HD, ei["g"],
+                                  ei["beta"], oe, Be, Te, H, D, D, chunk=C,
+                                  initial_state=ei["S0"], final_state=sTe, cu_seqlens=cu,
+                                  num_seqs=Se, stream=stream)
+            if events:
+                events[2].record(stream)
+            kda.kda_gated_norm(oe, ei["gate"], ei["norm_w"], yn, Ne, H, D, stream=stream)
+            if events:
+                events[3].record(stream)
+
+        for _ in range(args.warmup):
+            estep()
+        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            estep(eev[i])
+        torch.cuda.synchronize()
+        km = {n: sum(e[j].elapsed_time(e[j + 1]) for e in eev) / args.steps
+              for j, n in enumerate(("conv", "chunk", "norm"))}
+        ms = sum(km.values())
+        extra[es.name] = {"tokens": Ne, "sequences": Se, "ms_per_step": ms,
+                          "tokens_per_s": Ne / (ms * 1e-3), "kernels_ms": km}
+        log(f"{es.name}: {ms:.3f} ms/step, {Ne / ms / 1e3:.2f} M tokens/s")
+        del ei, ye, oe, yn, sTe
+    result["prefill_other_workloads"] = extra
+
     if not args.no_decode:
         dspec = synth.CONFIGS[4]
         B, Hd, Dd = dspec.B, dspec.H, dspec.D
