@@ -13,6 +13,7 @@ Pages cited:
   [CONV] "Inside Kimi K3" (lei.chat), KDA short-convolution diagram.
   [KDA]  "Inside Kimi K3" (lei.chat), Kimi Delta Attention one-head diagram.
   [MEM]  "Animated Kimi K3 architecture diagram" (github.io), local-memory panel.
+  [MLA]  "Inside Kimi K3" (lei.chat), gated multi-head latent attention diagram.
 """
 import numpy as np
 
@@ -211,3 +212,36 @@ def kda_decode_step(x, w, conv_state, g, beta, state, H, D, l2_eps=1e-6):
                                                state[b, h])
             o[b, h] = ob[0]
     return o, cs_new, S_new
+
+
+def mla_decode(q, w_uk, w_uv, cache, lengths, gate, scale=None):
+    """[MLA] one new token per sequence of gated multi-head latent attention,
+    read over the latent cache, straight from the diagram's moves: every
+    cached latent c_i is expanded into a key k_i = W_uk c_i and a value
+    v_i = W_uv c_i per head; the new token's query attends to all of them
+    (causal softmax of q . k_i, with the new token's own latent already in the
+    cache); the head output is the weighted sum of the values, times the
+    full-rank sigmoid gate.
+
+    q [B, H, Dk], w_uk [H, Dk, R], w_uv [H, Dv, R], cache [B, Lmax, R],
+    lengths [B] (cached tokens per sequence, >= 1), gate [B, H, Dv] logits.
+    The diagram prints no score scale; 1/sqrt(Dk) is taken.  Returns
+    y [B, H, Dv].
+    """
+    q = np.asarray(q, np.float64)
+    B, H, Dk = q.shape
+    Dv = w_uv.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dk)
+    y = np.zeros((B, H, Dv))
+    for b in range(B):
+        c = np.asarray(cache[b, :lengths[b]], np.float64)          # [L, R]
+        for h in range(H):
+            k = c @ np.asarray(w_uk[h], np.float64).T              # [L, Dk]
+            v = c @ np.asarray(w_uv[h], np.float64).T              # [L, Dv]
+            s = scale * (k @ q[b, h])                              # [L]
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ v
+            y[b, h] = o * sigmoid(np.asarray(gate[b, h], np.float64))
+    return y
