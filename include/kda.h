@@ -194,6 +194,44 @@ int kda_gated_norm(const void* o, const void* gate, const float* weight, void* y
                    int64_t n_tokens, int32_t H, int32_t D, float eps, int32_t dtype,
                    hipStream_t s);
 
+/*
+ * kda_mla_decode -- one decode step of gated multi-head latent attention over
+ * the latent cache.  ("Inside Kimi K3" (lei.chat), gated multi-head latent
+ * attention diagram: a 512-wide KV latent per token is cached; learned
+ * up-projections rebuild keys and values of 128 per head for 96 heads, no
+ * positional encoding; the new token's query takes a causal softmax over the
+ * cached tokens; the head output times a full-rank sigmoid gate.)
+ *
+ *   y[b,h,:] = sigmoid(gate[b,h,:]) * sum_i p_i W_uv[h] c_{b,i}
+ *   p = softmax_i(scale * q[b,h,:] . (W_uk[h] c_{b,i})),  i < lengths[b]
+ *
+ *   q        [B, H, Dk]        bf16 queries of the new token
+ *   w_uk     [H, Dk, R]        bf16 key up-projection (row d of head h)
+ *   w_uv     [H, Dv, R]        bf16 value up-projection
+ *   cache    [B, L_max, R]     bf16 latents c_i; the new token's own latent is
+ *                              already stored at position lengths[b] - 1
+ *   lengths  [B] int32 on the device: cached tokens per sequence, clamped to
+ *            [1, L_max]; rows at or past lengths[b] are never read
+ *   gate     [B, H, Dv]        bf16 gate logits (before the sigmoid)
+ *   y        [B, H, Dv]        bf16 output; overlaps no other tensor
+ *   workspace  device scratch of at least kda_mla_decode_workspace_bytes(B,
+ *              H, L_max) bytes, owned by the caller, disjoint from every
+ *              tensor; its contents on entry do not matter
+ *
+ * The key up-projection is folded into the query (q' = W_uk^T q, rounded to
+ * bf16) so all heads share one read of the cache; the value up-projection is
+ * applied after the softmax-weighted sum of latents.  This build supports
+ * dtype KDA_BF16, R = 512, Dk = Dv = 128 and H a multiple of 16 up to 96
+ * (others: KDA_ERR_UNSUPPORTED); scale must be finite and > 0.  B = 0 launches
+ * nothing and reads no pointer.  Calls that share a workspace must not overlap
+ * in time.
+ */
+int64_t kda_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t L_max);
+int kda_mla_decode(const void* q, const void* w_uk, const void* w_uv, const void* cache,
+                   const int32_t* lengths, const void* gate, void* y, void* workspace,
+                   int64_t workspace_bytes, int32_t B, int32_t H, int32_t L_max, int32_t R,
+                   int32_t Dk, int32_t Dv, float scale, int32_t dtype, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,8 @@ import os
 import torch
 
 __all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
-           "kda_decode_step", "kda_gated_norm", "kda_prefill", "KDA_F32", "KDA_BF16"]
+           "kda_decode_step", "kda_decode_multi", "kda_gated_norm", "kda_prefill",
+           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "KDA_F32", "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,8 +46,12 @@ def lib():
         L.kda_gated_norm.argtypes = [vp, vp, vp, vp, i64, i32, i32, f, i32, vp]
         L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        i32, f, vp]
+        L.kda_mla_decode_workspace_bytes.argtypes = [i32, i32, i32]
+        L.kda_mla_decode_workspace_bytes.restype = i64
+        L.kda_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
+                                     i32, f, i32, vp]
         for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
-                     "kda_decode_multi"):
+                     "kda_decode_multi", "kda_mla_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +174,36 @@ def kda_gated_norm(o, gate, weight, y, n_tokens, H, D, eps=1e-6, stream=None):
     _check("kda_gated_norm",
            lib().kda_gated_norm(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), n_tokens, H, D, eps,
                                 _dtype(o), _stream(stream)))
+
+
+def kda_mla_decode_workspace_bytes(B, H, L_max) -> int:
+    n = lib().kda_mla_decode_workspace_bytes(B, H, L_max)
+    if n < 0:
+        raise KdaError("kda_mla_decode_workspace_bytes", 1, kda_last_error())
+    return n
+
+
+def kda_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, workspace=None,
+                   scale=None, stream=None):
+    """One decode step of gated latent attention over the latent cache.
+    q [B, H, 128], w_uk / w_uv [H, 128, 512], cache [B, L_max, 512], lengths
+    [B] int32, gate / y [B, H, 128], all bf16 but lengths.  ``workspace`` is a
+    device byte tensor of at least kda_mla_decode_workspace_bytes(B, H, L_max)
+    bytes (None: one is allocated for this call).  scale defaults to
+    1/sqrt(128)."""
+    _same_dtype(q, w_uk, w_uv, cache, gate, y)
+    if lengths.dtype != torch.int32:
+        raise TypeError("lengths must be int32")
+    R, Dk, Dv = cache.shape[-1], q.shape[-1], w_uv.shape[-2]
+    if workspace is None:
+        workspace = torch.empty(max(kda_mla_decode_workspace_bytes(B, H, L_max), 1),
+                                dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = Dk ** -0.5
+    _check("kda_mla_decode",
+           lib().kda_mla_decode(_ptr(q), _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(lengths),
+                                _ptr(gate), _ptr(y), _ptr(workspace), workspace.numel(), B, H,
+                                L_max, R, Dk, Dv, scale, _dtype(q), _stream(stream)))
 
 
 def kda_prefill(x, w, g, beta, gate, norm_w, H, D, cu_seqlens=None, num_seqs=1, B=1, T=None,

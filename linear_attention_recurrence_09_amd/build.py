@@ -19,7 +19,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kda_api.cpp", "kda_norm.hip", "kda_conv.hip", "kda_decode.hip", "kda_chunk.hip",
-           "kda_chunk_pipe.hip"]
+           "kda_chunk_pipe.hip", "kda_mla.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -273,4 +273,63 @@ int kda_gated_norm(const void* o, const void* gate, const float* weight, void* y
     return hip_status(kda::launch_gated_norm(o, gate, weight, y, rows, D, eps, dtype, s), fn);
 }
 
+int64_t kda_mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t L_max) {
+    const char* fn = "kda_mla_decode_workspace_bytes";
+    if (B < 0 || H < 1 || L_max < 1) {
+        fail(KDA_ERR_INVALID_ARG, "%s: need B >= 0, H >= 1, L_max >= 1 (got %d, %d, %d)", fn, B, H,
+             L_max);
+        return -1;
+    }
+    return B == 0 ? 0 : kda::mla_workspace_bytes(B, H, L_max);
+}
+
+int kda_mla_decode(const void* q, const void* w_uk, const void* w_uv, const void* cache,
+                   const int32_t* lengths, const void* gate, void* y, void* workspace,
+                   int64_t workspace_bytes, int32_t B, int32_t H, int32_t L_max, int32_t R,
+                   int32_t Dk, int32_t Dv, float scale, int32_t dtype, hipStream_t s) {
+    const char* fn = "kda_mla_decode";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+    if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+    if (B > 65535) return fail(KDA_ERR_UNSUPPORTED, "%s: B must be <= 65535 (got %d)", fn, B);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (L_max < 1) return fail(KDA_ERR_INVALID_ARG, "%s: L_max must be >= 1 (got %d)", fn, L_max);
+    if (R < 1 || Dk < 1 || Dv < 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: R, Dk and Dv must be >= 1", fn);
+    if (R != 512 || Dk != 128 || Dv != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: needs R = 512, Dk = Dv = 128 (got %d, %d, %d)", fn, R,
+                    Dk, Dv);
+    if (H % 16 != 0 || H > 96)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 up to 96 (got %d)", fn, H);
+    if (!(scale > 0.f) || !(scale < 3.0e38f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    if (B == 0) return ok();   // nothing to read or write
+    if (q == nullptr || w_uk == nullptr || w_uv == nullptr || cache == nullptr ||
+        lengths == nullptr || gate == nullptr || y == nullptr || workspace == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: every pointer must be non-null", fn);
+    if (!aligned16(q) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
+        !aligned16(gate) || !aligned16(y))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(lengths) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: lengths must be 4-byte aligned", fn);
+    const int64_t need = kda::mla_workspace_bytes(B, H, L_max);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn,
+                    (long long)workspace_bytes, (long long)need);
+    const int64_t q_b = (int64_t)B * H * Dk * 2, wk_b = (int64_t)H * Dk * R * 2;
+    const int64_t wv_b = (int64_t)H * Dv * R * 2, c_b = (int64_t)B * L_max * R * 2;
+    const int64_t g_b = (int64_t)B * H * Dv * 2, y_b = g_b, l_b = (int64_t)B * 4;
+    if (overlap(y, y_b, q, q_b) || overlap(y, y_b, w_uk, wk_b) || overlap(y, y_b, w_uv, wv_b) ||
+        overlap(y, y_b, cache, c_b) || overlap(y, y_b, lengths, l_b) || overlap(y, y_b, gate, g_b) ||
+        overlap(y, y_b, workspace, need))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y must not overlap another tensor", fn);
+    if (overlap(workspace, need, q, q_b) || overlap(workspace, need, w_uk, wk_b) ||
+        overlap(workspace, need, w_uv, wv_b) || overlap(workspace, need, cache, c_b) ||
+        overlap(workspace, need, lengths, l_b) || overlap(workspace, need, gate, g_b))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
+    return hip_status(kda::launch_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, workspace, B,
+                                             H, L_max, scale, s),
+                      fn);
+}
+
 }  // extern "C"

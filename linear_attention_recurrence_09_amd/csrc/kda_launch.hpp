@@ -45,4 +45,13 @@ hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, con
                         const float* s0, float* sT, const int32_t* cu, int num_seqs, int T,
                         int H, int DK, int DV, int dtype, hipStream_t s);
 
+// Gated latent-attention decode step (kda_mla.hip): bf16, latent 512, heads of
+// 128, H a multiple of 16 up to 96.
+int mla_splits(int B, int Lmax);
+int64_t mla_workspace_bytes(int B, int H, int Lmax);
+hipError_t launch_mla_decode(const void* q, const void* w_uk, const void* w_uv,
+                             const void* cache, const int32_t* lengths, const void* gate, void* y,
+                             void* workspace, int B, int H, int Lmax, float scale,
+                             hipStream_t s);
+
 }  // namespace kda

@@ -22,6 +22,7 @@ import torch
 
 # tensor ids used to derive per-tensor seeds
 TID_X, TID_CONV_W, TID_G, TID_BETA, TID_GATE, TID_NORM_W, TID_S0, TID_CONV_STATE, TID_LENS = range(9)
+TID_Q, TID_W_UK, TID_W_UV, TID_CACHE = range(9, 13)
 
 
 @dataclass(frozen=True)
@@ -71,6 +72,25 @@ class DecodeSpec:
     seed: int = 1004
 
 
+@dataclass(frozen=True)
+class MlaSpec:
+    """One decode step of gated latent attention: B sequences with up to
+    L_max cached 512-wide latents, H heads of 128.  Cached lengths are L_max
+    for every sequence unless ``len_lo`` > 0 (then U[len_lo, L_max])."""
+    name: str
+    B: int
+    H: int
+    L_max: int
+    R: int = 512
+    Dh: int = 128
+    len_lo: int = 0
+    q_std: float = 1.0
+    w_std: float = 512 ** -0.5     # up-projections: unit-variance keys and values
+    cache_std: float = 1.0
+    gate_std: float = 1.0
+    seed: int = 3000
+
+
 # The five workloads of the measurement plan, plus stress variants that make
 # the inter-chunk carry visible (with g ~ U(-5, 0) a chunk forgets its
 # entering state almost completely).
@@ -84,6 +104,12 @@ CONFIGS = {
                    len_lo=512, len_hi=8192, varlen=True, s0_std=0.1, seed=1003),
     4: DecodeSpec("decode_B256_H96_D128_bf16_64steps", B=256, H=96, D=128, dtype="bf16", steps=64,
                   seed=1004),
+}
+
+# Latent-cache decode step of the global attention layers: the decode batch of
+# 256 sequences over a 4096-token cache.
+MLA = {
+    "decode": MlaSpec("mla_decode_B256_L4096_H96_R512_bf16", B=256, H=96, L_max=4096, seed=3001),
 }
 
 STRESS = {
@@ -191,3 +217,27 @@ def decode_inputs(spec: DecodeSpec, device="cpu", steps=None):
 def scaled(spec, **kw):
     """A copy of a spec with some fields replaced (smaller T, fewer heads...)."""
     return replace(spec, **kw)
+
+
+def mla_inputs(spec: MlaSpec, device="cpu", lengths=None):
+    """Draw one latent-attention decode step (all bf16 but ``lengths``):
+    q [B, H, Dh], w_uk / w_uv [H, Dh, R], cache [B, L_max, R], gate [B, H, Dh]
+    (logits), lengths [B] int32 on ``device`` (also as ``lengths_list``)."""
+    B, H, L, R, Dh, sd = spec.B, spec.H, spec.L_max, spec.R, spec.Dh, spec.seed
+    dt = torch.bfloat16
+    if lengths is None:
+        if spec.len_lo > 0:
+            lengths = torch.randint(spec.len_lo, L + 1, (B,), generator=_gen(sd, TID_LENS, "cpu"))
+            lengths = [int(v) for v in lengths]
+        else:
+            lengths = [L] * B
+    return dict(
+        spec=spec,
+        q=_normal((B, H, Dh), spec.q_std, 0.0, sd, TID_Q, device, dt),
+        w_uk=_normal((H, Dh, R), spec.w_std, 0.0, sd, TID_W_UK, device, dt),
+        w_uv=_normal((H, Dh, R), spec.w_std, 0.0, sd, TID_W_UV, device, dt),
+        cache=_normal((B, L, R), spec.cache_std, 0.0, sd, TID_CACHE, device, dt),
+        gate=_normal((B, H, Dh), spec.gate_std, 0.0, sd, TID_GATE, device, dt),
+        lengths=torch.tensor(lengths, dtype=torch.int32, device=device),
+        lengths_list=list(lengths),
+    )

@@ -20,7 +20,8 @@ MB = 1 << 20
 
 def declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(kda_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(kda_\w+)\s*\(", text,
+                                 re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +31,8 @@ def L():
 
 def test_header_declares_the_calls():
     assert declared() == ["kda_chunk_prefill", "kda_conv", "kda_decode_multi", "kda_decode_step",
-                          "kda_gated_norm", "kda_last_error", "kda_version"]
+                          "kda_gated_norm", "kda_last_error", "kda_mla_decode",
+                          "kda_mla_decode_workspace_bytes", "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -127,3 +129,44 @@ def test_decode_multi_argument_checks(L):
     assert dm(B=0) == OK
     assert dm(B=0, st_out=A + 5 * MB, cs_out=A + MB) == OK   # in place passes the checks
     assert dm(B=0, st_out=None, cs_out=None) == OK           # outputs only
+
+
+def test_mla_decode_argument_checks(L):
+    # B=2, H=96, L_max=64, bf16: the weights take 12 MB each, every other
+    # tensor and the workspace stay under 2 MB
+    B, H, Lm = 2, 96, 64
+    need = L.kda_mla_decode_workspace_bytes(B, H, Lm)
+    assert 0 < need < 2 * MB
+    assert L.kda_mla_decode_workspace_bytes(0, H, Lm) == 0
+    assert L.kda_mla_decode_workspace_bytes(B, 0, Lm) == -1
+    # more sequences or a longer cache never need less workspace
+    assert L.kda_mla_decode_workspace_bytes(256, H, 4096) >= L.kda_mla_decode_workspace_bytes(
+        128, H, 4096) >= L.kda_mla_decode_workspace_bytes(128, H, 32) > 0
+
+    def mla(q=A, wk=A + 32 * MB, wv=A + 64 * MB, c=A + 96 * MB, ln=A + 100 * MB, g=A + 102 * MB,
+            y=A + 104 * MB, ws=A + 106 * MB, wsb=None, B=B, H=H, Lm=Lm, R=512, Dk=128, Dv=128,
+            scale=0.088, dt=1):
+        return L.kda_mla_decode(q, wk, wv, c, ln, g, y, ws, need if wsb is None else wsb, B, H, Lm,
+                                R, Dk, Dv, scale, dt, None)
+    assert mla(q=None) == INVALID
+    assert mla(ws=None) == INVALID
+    assert mla(dt=0) == UNSUPPORTED                          # fp32 is not implemented
+    assert mla(dt=7) == INVALID
+    assert mla(H=48 + 8) == UNSUPPORTED                      # not a multiple of 16
+    assert mla(H=112) == UNSUPPORTED
+    assert mla(R=256) == UNSUPPORTED
+    assert mla(Dk=64) == UNSUPPORTED
+    assert mla(Lm=0) == INVALID
+    assert mla(B=-1) == INVALID
+    assert mla(scale=0.0) == INVALID
+    assert mla(scale=float("inf")) == INVALID
+    assert mla(scale=float("nan")) == INVALID
+    assert mla(wsb=need - 1) == INVALID                      # workspace too small
+    assert mla(y=A + 16) == INVALID                          # y overlaps q
+    assert mla(y=A + 106 * MB) == INVALID                    # y overlaps the workspace
+    assert mla(ws=A + 96 * MB + 64) == INVALID               # workspace over the cache
+    assert mla(c=A + 96 * MB + 8) == INVALID                 # misaligned cache
+    assert mla(ln=A + 100 * MB + 2) == INVALID               # misaligned lengths
+    assert "kda_mla_decode" in kda.kda_last_error()
+    assert mla(B=0, wsb=0) == OK
+    assert mla(B=0, wsb=0, q=None, ws=None) == OK            # an empty batch reads no pointer
