@@ -105,6 +105,58 @@ def decode_multi_bytes(B, K, H, D, es=2, write_states=True, outputs=True):
             + P * 4 * 4)                               # conv weights
 
 
+def mla_bytes(B, H, L, R=512, Dh=128, es=2):
+    """Algorithmic HBM bytes of one latent-attention decode step: the cached
+    latents once, both up-projections, the query, gate and output (the split
+    partials in the workspace are the kernel's own, not counted)."""
+    return B * L * R * es + 2 * H * Dh * R * es + 3 * B * H * Dh * es
+
+
+def mla_flops(B, H, L, R=512, Dh=128):
+    """Scores q'.c and the weighted latent sum (2 R each per head and cached
+    token), plus the two per-head projections q' = W_uk^T q and o = W_uv u."""
+    return B * H * (4 * L * R + 4 * Dh * R)
+
+
+def bench_mla(kda, synth, torch, stream, reps):
+    """One latent-attention decode step over a 4096-token latent cache for
+    256 sequences and 96 heads, timed with HIP events on the launch stream."""
+    spec = synth.MLA["decode"]
+    B, H, L = spec.B, spec.H, spec.L_max
+    log(f"drawing inputs for {spec.name}")
+    inp = synth.mla_inputs(spec, device="cuda")
+    y = torch.empty((B, H, spec.Dh), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(kda.kda_mla_decode_workspace_bytes(B, H, L), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        kda.kda_mla_decode(inp["q"], inp["w_uk"], inp["w_uv"], inp["cache"], inp["lengths"],
+                           inp["gate"], y, B, H, L, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    med = per[len(per) // 2]
+    nb, fl = mla_bytes(B, H, L), mla_flops(B, H, L)
+    log(f"mla decode: {med:.3f} ms/step, {nb / med / 1e9:.2f} TB/s")
+    del inp, y, ws
+    return {"workload": spec.name, "B": B, "H": H, "L": L, "R": spec.R,
+            "ms_per_step_median": med, "ms_per_step_min": per[0], "ms_per_step_max": per[-1],
+            "bytes_per_step": nb, "TBps": nb / (med * 1e-3) / 1e12,
+            "hbm_frac": nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops_algorithmic": fl / (med * 1e-3) / 1e12,
+            "mfma_frac": fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "tokens_per_s": B / (med * 1e-3)}
+
+
 def cpu_baseline(inp, spec, T_s, H_s):
     """Oracle on the first T_s tokens of the first H_s heads (all its threads)."""
     import numpy as np
@@ -219,13 +271,15 @@ def main():
                                  conv_state_out=cs, state_out=S, stream=stream)
         torch.cuda.synchronize()
         del d, cs, S, xb, gb, bb, om
+        # three latent-attention decode steps (256 x 4096 cached latents)
+        bench_mla(kda, synth, torch, stream, reps=3)
         src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         log("counter run done: conv, 3 chunk launches, norm, 3 decode steps, 2 four-token "
-            "decode calls, 3 copies of 2 GiB")
+            "decode calls, 6 latent-attention decode steps, 3 copies of 2 GiB")
         return
 
     for _ in range(args.warmup):
@@ -427,6 +481,9 @@ def main():
                 "bytes": decode_multi_bytes(B, K, Hd, Dd, write_states=False)
                          + decode_multi_bytes(B, K, Hd, Dd, outputs=False)}}
         del d, cs, S
+
+    if not args.no_decode:
+        result["mla_decode"] = bench_mla(kda, synth, torch, stream, reps=max(args.steps, 10))
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
