@@ -31,10 +31,6 @@ namespace {
 constexpr int kR = 512;            // latent width
 constexpr int kDh = 128;           // key / value width per head
 constexpr int kTL = 32;            // cached tokens per attention tile
-constexpr int kAttnThreads = 512;  // 8 waves
-constexpr int kRP = kR + 16;       // LDS row pitch (bf16) of Q' and the cache tile: 8 banks per row
-constexpr int kPP = kTL + 8;       // LDS row pitch (bf16) of P
-constexpr int kSP = kTL + 1;       // LDS row pitch (fp32) of S
 constexpr int kSeqPerBlock = 8;    // sequences per absorb / combine workgroup
 
 typedef __bf16 bf16v4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
@@ -77,23 +73,41 @@ mla_absorb_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ w_uk,
 }
 
 // ---- 2. attention over one range of the cache, all heads ------------------
-// Workgroup (split sp, sequence b), 8 waves.  Head tiles of 16 (HT of them);
-// S tiles (head tile, 16 tokens) are dealt to the waves; U is held in
-// registers, wave w owning latent columns 64 w .. 64 w + 63 of every head.
+// Workgroup (split sp, sequence b), 2 HT waves.  Wave w works for head tile
+// ht = w / 2 (16 heads) and half h = w % 2: it holds the Q' rows of its heads
+// for latent channels 256 h .. +255 in registers, and owns latent columns
+// 256 h .. +255 of U.  Per tile of 32 cached tokens:
+//  * each wave forms its half of the scores over its 256 channels; the two
+//    halves are summed through LDS (x + y in one wave, y + x in the other:
+//    both hold bitwise the same scores, hence the same softmax);
+//  * U += P C over the wave's columns.
+// Scores are formed transposed, S^T = C Q'^T (tokens x heads): lane (q, c)
+// holds head c at tokens 4q .. 4q+3 of each 16-token half of the tile.  Read
+// as the A operand of U += P C (rows = heads), those eight values sit at
+// k = 8q .. 8q+7, so the K index of that product runs over the tokens in the
+// order {4q .. 4q+3, 16+4q .. 16+4q+3}; the B operand (the tile as [token]
+// [column]) is read in the same order by two transposed reads.  Softmax: a
+// running max per head (base 2: q' carries log2 e); row sums stay per lane
+// until the end.
+// Cache tiles stream through registers a step ahead into two LDS stages.
+constexpr int kCP = kR * 2 + 16;            // LDS row pitch (bytes) of a cache tile: 4 banks between rows
+
 template <int HT>
-__global__ void __launch_bounds__(kAttnThreads)
+__global__ void __launch_bounds__(128 * HT)
 mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
                 const int32_t* __restrict__ lengths, float* __restrict__ part_ml,
                 float* __restrict__ part_u, int Lmax, int nsplit) {
-    constexpr int H = 16 * HT;
-    __shared__ __attribute__((aligned(16))) __bf16 sQ[H * kRP];
-    __shared__ __attribute__((aligned(16))) __bf16 sC[kTL * kRP];
-    __shared__ __attribute__((aligned(16))) float sS[H * kSP];
-    __shared__ __attribute__((aligned(16))) __bf16 sP[H * kPP];
-    __shared__ __attribute__((aligned(16))) float sAlpha[H];
+    constexpr int H = 16 * HT, NW = 2 * HT;
+    constexpr int RPW = (kTL + NW - 1) / NW;   // cache rows loaded per wave and tile
+    constexpr int SROWS = NW * RPW;            // rows of a stage (those past the tile are padding)
+    __shared__ __attribute__((aligned(16))) char sC[2][SROWS * kCP];
+    __shared__ __attribute__((aligned(16))) floatx4 sX[NW][2][64];   // partial scores
+    __shared__ __attribute__((aligned(16))) float sA[NW][16];        // rescale factors
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
+    const int ht = wave >> 1, hf = wave & 1;
     const int sp = blockIdx.x, b = blockIdx.y;
     int L = lengths[b];
     L = L < 1 ? 1 : (L > Lmax ? Lmax : L);
@@ -102,127 +116,142 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
     const int t_lo = sp * tps;
     const int t_hi = t_lo + tps < tiles ? t_lo + tps : tiles;
 
-    // Q' of this sequence into LDS (rows of 512 bf16 = 64 x 16 bytes)
-    const __bf16* qb = qp + (int64_t)b * H * kR;
-    for (int i = tid; i < H * (kR / 8); i += kAttnThreads) {
-        const int row = i / (kR / 8), c8 = i % (kR / 8);
-        *reinterpret_cast<bf16x8*>(&sQ[row * kRP + 8 * c8]) =
-            *reinterpret_cast<const bf16x8*>(qb + (int64_t)row * kR + 8 * c8);
-    }
-    // the cache tile: 32 rows x 64 pieces of 16 bytes, 4 per thread; rows
-    // past the sequence's length read as zeros (their scores are masked)
-    const __bf16* cb = cache + (int64_t)b * Lmax * kR;
-    bf16x8 pre[4];
-    auto fetch = [&](int t) {
+    // Q'^T as B operands over this wave's channels (lane (q, c): head
+    // ht*16 + c, k = 256 hf + 32 ks + 8q .. +7)
+    const __bf16* qrow = qp + ((int64_t)b * H + ht * 16 + lr) * kR + 256 * hf + 8 * lq;
+    bf16x8 qb[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int id = tid + kAttnThreads * j, row = id / (kR / 8), c8 = id % (kR / 8);
-            const int tok = t * kTL + row;
-            pre[j] = tok < L ? *reinterpret_cast<const bf16x8*>(cb + (int64_t)tok * kR + 8 * c8)
-                             : bf16x8{};
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    // complete them here: otherwise the tile loop's first products wait on
+    // the memory counter, which then also holds back the cache prefetch
+    asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]), "v"(qb[4]), "v"(qb[5]),
+                 "v"(qb[6]), "v"(qb[7]));
+
+    // rows wave + NW j of a tile, 16 bytes per lane.  Every wave loads and
+    // stores the same number of rows with no branch (so the compiler counts
+    // the loads in flight exactly): rows past the tile land in the stage's
+    // padding rows, rows past the length repeat the last valid row (their
+    // scores are masked), and tiles past the range repeat the last tile
+    // (never used), so every load is in bounds.
+    const __bf16* cb = cache + (int64_t)b * Lmax * kR + 8 * lane;
+    auto fetch = [&](bf16x8 (&r)[RPW], int t) {
+        const int tc = t < t_hi ? t : t_hi - 1;
+#pragma unroll
+        for (int j = 0; j < RPW; ++j) {
+            const int row = wave + NW * j;
+            int tok = tc * kTL + (row < kTL ? row : kTL - 1);
+            tok = tok < L ? tok : L - 1;
+            r[j] = *reinterpret_cast<const bf16x8*>(cb + (int64_t)tok * kR);
         }
     };
-    auto stage = [&]() {
+    auto put = [&](const bf16x8 (&r)[RPW], char* st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int id = tid + kAttnThreads * j, row = id / (kR / 8), c8 = id % (kR / 8);
-            *reinterpret_cast<bf16x8*>(&sC[row * kRP + 8 * c8]) = pre[j];
-        }
+        for (int j = 0; j < RPW; ++j)
+            *reinterpret_cast<bf16x8*>(st + (wave + NW * j) * kCP + 16 * lane) = r[j];
     };
 
-    // running softmax state, one thread per head (base 2: q' carries log2 e)
-    float m_run = -__builtin_inff(), l_run = 0.f;
-    floatx4 U[HT][4];
+    float m_ref = -__builtin_inff();   // per head (lane's c), identical over q
+    float l_part = 0.f;                // this lane's share of the row sum
+    floatx4 U[16];                     // lane (q, c): heads 4q+i, column 256 hf + 16 j + c
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) U[ht][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 16; ++j) U[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    if (t_lo < t_hi) fetch(t_lo);
-    for (int t = t_lo; t < t_hi; ++t) {
-        __syncthreads();   // the previous tile's reads of sC, sP, sAlpha are done
-        stage();
-        if (t + 1 < t_hi) fetch(t + 1);   // in flight while this tile computes
+    // one tile on stage st; afterwards tile t + 2 (in flight in r since the
+    // previous step) goes into st and r is refilled with tile t + 3
+    auto step = [&](int t, char* st, bf16x8 (&r)[RPW]) {
+        // this wave's half of S^T = C Q'^T for the two 16-token halves
+        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int off = (256 * hf + 32 * ks + 8 * lq) * 2;
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + lr * kCP + off);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + (16 + lr) * kCP + off);
+            s0 = mla_mfma32(a0, qb[ks], s0);
+            s1 = mla_mfma32(a1, qb[ks], s1);
+            if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+        }
+        sX[wave][0][lane] = s0;
+        sX[wave][1][lane] = s1;
+        __syncthreads();   // both halves of every head tile's scores are in LDS
+        s0 += sX[wave ^ 1][0][lane];
+        s1 += sX[wave ^ 1][1][lane];
+        // mask tokens past the length (only the last tile has any)
+        const int base = t * kTL + 4 * lq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (base + i >= L) s0[i] = -__builtin_inff();
+            if (base + 16 + i >= L) s1[i] = -__builtin_inff();
+        }
+        float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        // running max per head; U and the partial sums are rescaled every
+        // tile (the factor is 1 where the max did not move, 0 on the first
+        // tile, where m_ref starts at -inf)
+        {
+            const float m_new = fmaxf(m_ref, mt);
+            const float alpha = fast_exp2(m_ref - m_new);
+            m_ref = m_new;
+            l_part *= alpha;
+            // U's rows are heads 4q .. 4q+3: gather their factors
+            if (lq == 0) sA[wave][lr] = alpha;
+            __builtin_amdgcn_wave_barrier();
+            const floatx4 al = *reinterpret_cast<const floatx4*>(&sA[wave][4 * lq]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U[j][i] *= al[i];
+            __builtin_amdgcn_wave_barrier();
+        }
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(s0[i] - m_ref);
+            p[4 + i] = fast_exp2(s1[i] - m_ref);
+        }
+        l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        const bf16x8 pa = __builtin_convertvector(floatx8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]}, bf16x8);
+
+        // U += P C over this wave's 256 latent columns
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int col = 256 * hf + 16 * j + 4 * (lr & 3);
+            const bf16v4 lo = mla_read_tr(reinterpret_cast<const __bf16*>(st + (4 * lq + (lr >> 2)) * kCP + col * 2));
+            const bf16v4 hi = mla_read_tr(reinterpret_cast<const __bf16*>(st + (16 + 4 * lq + (lr >> 2)) * kCP + col * 2));
+            const bf16x8 cf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            U[j] = mla_mfma32(pa, cf, U[j]);
+            if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+        }
+        __syncthreads();   // every wave is done with this stage and with sX
+        put(r, st);        // tile t + 2
+        fetch(r, t + 3);
+    };
+
+    bf16x8 ra[RPW];
+    if (t_lo < t_hi) {
+        fetch(ra, t_lo);
+        put(ra, sC[0]);
+        fetch(ra, t_lo + 1);
+        put(ra, sC[1]);
+        fetch(ra, t_lo + 2);
         __syncthreads();
-
-        // S = Q' C^T, tiles (head tile, token tile) dealt to the waves
-        for (int st = wave; st < 2 * HT; st += kAttnThreads / 64) {
-            const int ht = st >> 1, tt = st & 1;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < kR / 32; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sQ[(ht * 16 + lr) * kRP + 32 * ks + 8 * lq]);
-                const bf16x8 c = *reinterpret_cast<const bf16x8*>(&sC[(tt * 16 + lr) * kRP + 32 * ks + 8 * lq]);
-                acc = mla_mfma32(a, c, acc);
-            }
-            // lane (q, c): heads ht*16 + 4q + i, token tt*16 + c
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sS[(ht * 16 + 4 * lq + i) * kSP + tt * 16 + lr] = acc[i];
-        }
-        __syncthreads();
-
-        // online softmax, one thread per head
-        if (tid < H) {
-            const int valid = L - t * kTL < kTL ? L - t * kTL : kTL;
-            float sc[kTL];
-            float mt = -__builtin_inff();
-#pragma unroll
-            for (int j = 0; j < kTL; ++j) {
-                sc[j] = j < valid ? sS[tid * kSP + j] : -__builtin_inff();
-                mt = fmaxf(mt, sc[j]);
-            }
-            const float m_new = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
-            float sum = 0.f;
-#pragma unroll
-            for (int j = 0; j < kTL; j += 2) {
-                const float p0 = fast_exp2(sc[j] - m_new), p1 = fast_exp2(sc[j + 1] - m_new);
-                sum += p0 + p1;
-                *reinterpret_cast<bf16x2*>(&sP[tid * kPP + j]) =
-                    __builtin_convertvector(floatx2{p0, p1}, bf16x2);
-            }
-            l_run = l_run * alpha + sum;
-            m_run = m_new;
-            sAlpha[tid] = alpha;
-        }
-        __syncthreads();
-
-        // U = diag(alpha) U + P C: wave w holds latent columns 64 w .. 64 w + 63
-        bf16x8 cf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // B operand: tokens 8q .. 8q+7 of latent column 64 w + 16 j + lr
-            const int n0 = 64 * wave + 16 * j;
-            const bf16v4 lo = mla_read_tr(&sC[(8 * lq + (lr >> 2)) * kRP + n0 + 4 * (lr & 3)]);
-            const bf16v4 hi = mla_read_tr(&sC[(8 * lq + 4 + (lr >> 2)) * kRP + n0 + 4 * (lr & 3)]);
-            cf[j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&sP[(ht * 16 + lr) * kPP + 8 * lq]);
-            const floatx4 al = *reinterpret_cast<const floatx4*>(&sAlpha[ht * 16 + 4 * lq]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) U[ht][j][i] *= al[i];
-                U[ht][j] = mla_mfma32(pa, cf[j], U[ht][j]);
-            }
-        }
     }
+    for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) & 1], ra);
 
     // partial results of this split: m, l per head; U [H][512]
+    float l_head = l_part + __shfl_xor(l_part, 16, 64);
+    l_head += __shfl_xor(l_head, 32, 64);
     const int64_t pb = ((int64_t)b * nsplit + sp) * H;
-    if (tid < H) {
-        part_ml[(pb + tid) * 2] = m_run;
-        part_ml[(pb + tid) * 2 + 1] = l_run;
+    if (hf == 0 && lq == 0) {
+        part_ml[(pb + ht * 16 + lr) * 2] = m_ref;
+        part_ml[(pb + ht * 16 + lr) * 2 + 1] = l_head;
     }
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part_u[(pb + ht * 16 + 4 * lq + i) * kR + 64 * wave + 16 * j + lr] = U[ht][j][i];
+        for (int i = 0; i < 4; ++i)
+            part_u[(pb + ht * 16 + 4 * lq + i) * kR + 256 * hf + 16 * j + lr] = U[j][i];
 }
 
 // ---- 3. combine the splits, o = W_uv u, y = o * sigmoid(gate) -------------
@@ -285,7 +314,7 @@ template <int HT>
 hipError_t launch_attn_t(const void* qp, const void* cache, const int32_t* lengths, float* ml,
                          float* pu, int B, int Lmax, int nsplit, hipStream_t s) {
     hipLaunchKernelGGL((mla_attn_kernel<HT>), dim3((unsigned)nsplit, (unsigned)B),
-                       dim3(kAttnThreads), 0, s, (const __bf16*)qp, (const __bf16*)cache, lengths,
+                       dim3(128 * HT), 0, s, (const __bf16*)qp, (const __bf16*)cache, lengths,
                        ml, pu, Lmax, nsplit);
     return hipGetLastError();
 }
