@@ -31,7 +31,6 @@ namespace {
 constexpr int kR = 512;            // latent width
 constexpr int kDh = 128;           // key / value width per head
 constexpr int kTL = 32;            // cached tokens per attention tile
-constexpr int kSeqPerBlock = 8;    // sequences per absorb / combine workgroup
 
 typedef __bf16 bf16v4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
@@ -47,29 +46,72 @@ __device__ __forceinline__ bf16v4 mla_read_tr(const __bf16* p) {
 }
 
 // ---- 1. absorb: q'[b][h][r] = s * sum_d q[b][h][d] W_uk[h][d][r] ----------
-__global__ void __launch_bounds__(kR)
+// Workgroup (head h, 32 sequences), 4 waves: a 32 x 512 x 128 product on
+// 16x16x32 MFMA.  W_uk[h] (128 x 512) is staged in LDS and read as the B
+// operand by transposed reads (K = d runs down its columns); q rows are the
+// A operand, straight from memory.  Wave w owns latent columns 128 w .. +127.
+constexpr int kGS = 32;            // sequences per absorb / combine workgroup
+constexpr int kWP = kR * 2 + 16;   // LDS row pitch (bytes) of W_uk[h]: 4 banks between rows
+__global__ void __launch_bounds__(256)
 mla_absorb_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ w_uk,
                   __bf16* __restrict__ qp, int B, int H, float s) {
-    __shared__ float sq[kSeqPerBlock][kDh];
-    const int h = blockIdx.x, b0 = blockIdx.y * kSeqPerBlock, r = threadIdx.x;
-    const int nb = B - b0 < kSeqPerBlock ? B - b0 : kSeqPerBlock;
-    for (int i = threadIdx.x; i < kSeqPerBlock * kDh; i += kR) {
-        const int j = i / kDh, d = i % kDh;
-        sq[j][d] = j < nb ? (float)q[((int64_t)(b0 + j) * H + h) * kDh + d] : 0.f;
+    __shared__ __attribute__((aligned(16))) char sW[kDh * kWP];
+    const int h = blockIdx.x, b0 = blockIdx.y * kGS, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lq = lane >> 4;
+    // all 32 loads of this thread's share of W_uk[h] in flight at once
+    const __bf16* wh = w_uk + (int64_t)h * kDh * kR;
+    constexpr int kWL = kDh * (kR / 8) / 256;
+    bf16x8 wt[kWL];
+#pragma unroll
+    for (int j = 0; j < kWL; ++j) {
+        const int i = tid + 256 * j, d = i / (kR / 8), c8 = i % (kR / 8);
+        wt[j] = *reinterpret_cast<const bf16x8*>(wh + (int64_t)d * kR + 8 * c8);
+    }
+#pragma unroll
+    for (int j = 0; j < kWL; ++j) {
+        const int i = tid + 256 * j, d = i / (kR / 8), c8 = i % (kR / 8);
+        *reinterpret_cast<bf16x8*>(sW + d * kWP + 16 * c8) = wt[j];
+    }
+    // A operands: rows b0 + 16 mt + lr (rows past B read row B - 1, never stored)
+    bf16x8 qa[2][kDh / 32];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        int bb = b0 + 16 * mt + lr;
+        bb = bb < B ? bb : B - 1;
+        const __bf16* qr = q + ((int64_t)bb * H + h) * kDh + 8 * lq;
+#pragma unroll
+        for (int ks = 0; ks < kDh / 32; ++ks) qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qr + 32 * ks);
     }
     __syncthreads();
-    float acc[kSeqPerBlock];
+    floatx4 acc[2][8];
 #pragma unroll
-    for (int j = 0; j < kSeqPerBlock; ++j) acc[j] = 0.f;
-    const __bf16* wh = w_uk + (int64_t)h * kDh * kR + r;
-    for (int d = 0; d < kDh; ++d) {
-        const float wv = (float)wh[(int64_t)d * kR];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int j = 0; j < kSeqPerBlock; ++j) acc[j] += sq[j][d] * wv;
-    }
+        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kSeqPerBlock; ++j)
-        if (j < nb) qp[((int64_t)(b0 + j) * H + h) * kR + r] = (__bf16)(acc[j] * s);
+    for (int ks = 0; ks < kDh / 32; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            // B operand: rows d = 32 ks + 8q .. +7 of column 128 w + 16 nt + lane
+            const int col = 128 * wave + 16 * nt + 4 * (lr & 3);
+            const bf16v4 lo = mla_read_tr(reinterpret_cast<const __bf16*>(sW + (32 * ks + 8 * lq + (lr >> 2)) * kWP + col * 2));
+            const bf16v4 hi = mla_read_tr(reinterpret_cast<const __bf16*>(sW + (32 * ks + 8 * lq + 4 + (lr >> 2)) * kWP + col * 2));
+            const bf16x8 wb = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            acc[0][nt] = mla_mfma32(qa[0][ks], wb, acc[0][nt]);
+            acc[1][nt] = mla_mfma32(qa[1][ks], wb, acc[1][nt]);
+        }
+    // lane (q, c): sequences b0 + 16 mt + 4q + i, latent column 128 w + 16 nt + c
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int bb = b0 + 16 * mt + 4 * lq + i;
+            if (bb < B) {
+                __bf16* out = qp + ((int64_t)bb * H + h) * kR + 128 * wave + lr;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) out[16 * nt] = (__bf16)(acc[mt][nt][i] * s);
+            }
+        }
 }
 
 // ---- 2. attention over one range of the cache, all heads ------------------
@@ -255,59 +297,106 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
 }
 
 // ---- 3. combine the splits, o = W_uv u, y = o * sigmoid(gate) -------------
+// Workgroup (head h, 32 sequences), 4 waves.  The splits are merged into
+// u = sum_s U_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) (fp32, rounded to bf16 in
+// LDS), then o = u W_uv[h]^T (32 x 128 x 512) on 16x16x32 MFMA: u rows are
+// the A operand, rows of W_uv[h] the B operand straight from memory (K = the
+// latent index runs along them).  Wave w owns output columns 32 w .. +31.
+constexpr int kUP = kR * 2 + 16;   // LDS row pitch (bytes) of u
 __global__ void __launch_bounds__(256)
 mla_combine_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_u,
                    const __bf16* __restrict__ w_uv, const __bf16* __restrict__ gate,
                    __bf16* __restrict__ y, int B, int H, int nsplit) {
-    __shared__ float su[kSeqPerBlock][kR];
-    __shared__ float so[2][kSeqPerBlock][kDh];
-    const int h = blockIdx.x, b0 = blockIdx.y * kSeqPerBlock, tid = threadIdx.x;
-    const int nb = B - b0 < kSeqPerBlock ? B - b0 : kSeqPerBlock;
-    // u = sum_s U_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
-    for (int i = tid; i < kSeqPerBlock * kR; i += 256) {
-        const int j = i / kR, r = i % kR;
-        float val = 0.f;
-        if (j < nb) {
-            const int64_t base = (int64_t)(b0 + j) * nsplit * H + h;
-            float M = -__builtin_inff();
-            for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(base + (int64_t)s * H) * 2]);
-            float num = 0.f, den = 0.f;
-            for (int s = 0; s < nsplit; ++s) {
-                const int64_t ps = base + (int64_t)s * H;
-                const float ws = fast_exp2(part_ml[ps * 2] - M);   // 0 for an empty split
-                den += ws * part_ml[ps * 2 + 1];
-                num += ws * part_u[ps * kR + r];
+    __shared__ __attribute__((aligned(16))) char su[kGS * kUP];
+    const int h = blockIdx.x, b0 = blockIdx.y * kGS, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lq = lane >> 4;
+    const int nb = B - b0 < kGS ? B - b0 : kGS;
+    // this wave's B operands (rows 32 w + lr and 32 w + 16 + lr of W_uv[h]),
+    // all in flight while the splits are merged
+    const __bf16* wr = w_uv + ((int64_t)h * kDh + 32 * wave + lr) * kR + 8 * lq;
+    bf16x8 wv[kR / 32][2];
+#pragma unroll
+    for (int ks = 0; ks < kR / 32; ++ks) {
+        wv[ks][0] = *reinterpret_cast<const bf16x8*>(wr + 32 * ks);
+        wv[ks][1] = *reinterpret_cast<const bf16x8*>(wr + 16 * kR + 32 * ks);
+    }
+    // merge the splits: wave w takes sequences b0 + 8 w .. +7, lane l latent
+    // columns 8 l .. 8 l + 7; splits outermost, so each split's loads for
+    // all eight sequences are in flight together
+    float M[8], den[8], num[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        M[j] = -__builtin_inff();
+        den[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[j][e] = 0.f;
+    }
+    const int j0 = 8 * wave;
+    auto row_of = [&](int j) -> int64_t {   // sequences past B reuse b0's rows (never stored)
+        const int bb = b0 + j0 + j < B ? b0 + j0 + j : b0;
+        return (int64_t)bb * nsplit * H + h;
+    };
+    for (int sp = 0; sp < nsplit; ++sp)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) M[j] = fmaxf(M[j], part_ml[(row_of(j) + (int64_t)sp * H) * 2]);
+    for (int sp = 0; sp < nsplit; ++sp) {
+        floatx4 pu[8][2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float* src = part_u + (row_of(j) + (int64_t)sp * H) * kR + 8 * lane;
+            pu[j][0] = *reinterpret_cast<const floatx4*>(src);
+            pu[j][1] = *reinterpret_cast<const floatx4*>(src + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t ps = row_of(j) + (int64_t)sp * H;
+            const float ws = fast_exp2(part_ml[ps * 2] - M[j]);   // 0 for an empty split
+            den[j] += ws * part_ml[ps * 2 + 1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                num[j][e] += ws * pu[j][0][e];
+                num[j][4 + e] += ws * pu[j][1][e];
             }
-            val = num / den;
         }
-        su[j][r] = val;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float inv = j0 + j < nb ? 1.f / den[j] : 0.f;
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)(num[j][e] * inv);
+        *reinterpret_cast<bf16x8*>(su + (j0 + j) * kUP + 16 * lane) = v;
     }
     __syncthreads();
-    // o[j][d]: thread (d, half) sums latent columns 256 half .. +255
-    const int d = tid & (kDh - 1), half = tid >> 7;
-    float acc[kSeqPerBlock];
+    floatx4 acc[2][2];
 #pragma unroll
-    for (int j = 0; j < kSeqPerBlock; ++j) acc[j] = 0.f;
-    const __bf16* wr = w_uv + ((int64_t)h * kDh + d) * kR + 256 * half;
-    for (int r8 = 0; r8 < 256; r8 += 8) {
-        const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wr + r8);
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float wf = (float)wv[e];
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < kSeqPerBlock; ++j) acc[j] += wf * su[j][256 * half + r8 + e];
-        }
+    for (int ks = 0; ks < kR / 32; ++ks) {
+        const bf16x8 w0 = wv[ks][0], w1 = wv[ks][1];
+        const bf16x8 u0 = *reinterpret_cast<const bf16x8*>(su + lr * kUP + (32 * ks + 8 * lq) * 2);
+        const bf16x8 u1 = *reinterpret_cast<const bf16x8*>(su + (16 + lr) * kUP + (32 * ks + 8 * lq) * 2);
+        acc[0][0] = mla_mfma32(u0, w0, acc[0][0]);
+        acc[0][1] = mla_mfma32(u0, w1, acc[0][1]);
+        acc[1][0] = mla_mfma32(u1, w0, acc[1][0]);
+        acc[1][1] = mla_mfma32(u1, w1, acc[1][1]);
     }
+    // lane (q, c): sequences b0 + 16 mt + 4q + i, output column 32 w + 16 nt + c
 #pragma unroll
-    for (int j = 0; j < kSeqPerBlock; ++j) so[half][j][d] = acc[j];
-    __syncthreads();
-    if (tid < kDh) {
-        for (int j = 0; j < nb; ++j) {
-            const int64_t o = ((int64_t)(b0 + j) * H + h) * kDh + tid;
-            const float z = (float)gate[o];
-            y[o] = (__bf16)((so[0][j][tid] + so[1][j][tid]) * sigmoidf_(z));
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int bb = b0 + 16 * mt + 4 * lq + i;
+            if (bb < B) {
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int64_t o = ((int64_t)bb * H + h) * kDh + 32 * wave + 16 * nt + lr;
+                    y[o] = (__bf16)(acc[mt][nt][i] * sigmoidf_((float)gate[o]));
+                }
+            }
         }
-    }
 }
 
 template <int HT>
@@ -345,8 +434,8 @@ hipError_t launch_mla_decode(const void* q, const void* w_uk, const void* w_uv,
     __bf16* qp = reinterpret_cast<__bf16*>(ws);
     float* ml = reinterpret_cast<float*>(ws + (int64_t)B * H * kR * 2);
     float* pu = ml + (int64_t)B * ns * H * 2;
-    const dim3 grid_bh((unsigned)H, (unsigned)((B + kSeqPerBlock - 1) / kSeqPerBlock));
-    hipLaunchKernelGGL(mla_absorb_kernel, grid_bh, dim3(kR), 0, s, (const __bf16*)q,
+    const dim3 grid_bh((unsigned)H, (unsigned)((B + kGS - 1) / kGS));
+    hipLaunchKernelGGL(mla_absorb_kernel, grid_bh, dim3(256), 0, s, (const __bf16*)q,
                        (const __bf16*)w_uk, qp, B, H, scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
