@@ -11,7 +11,8 @@ Inputs (CSV files written by the commands recorded in the summaries):
   --write  <dir>/write_counter_collection.csv from
            rocprofv3 --pmc WRITE_SIZE -T -f csv -d <dir> -o write -- python3 bench.py --counters
 
-Writes profiles/chunk_prefill_T65536_kernel_stats.txt,
+Writes profiles/chunk_prefill_T65536_kernel_stats.txt (every kernel of the
+run, the latent-attention decode kernels included),
 profiles/chunk_prefill_T65536_traffic.json and, for every kernel of the
 counter run, profiles/kernels_traffic_T65536_B256.txt.  The byte counters (KiB per
 dispatch) are scaled by what the same counter reads for bench.py's copy
@@ -114,7 +115,7 @@ def main():
     # kernel-trace statistics
     rows = list(csv.DictReader(open(args.trace)))
     lines = ["# rocprofv3 kernel statistics of one bench.py run (prefill T=65536, H=96, D=128,",
-             "# bf16 I/O; decode B=256 x 64 steps), MI355X",
+             "# bf16 I/O; decode B=256 x 64 steps; latent-attention decode B=256 x 4096), MI355X",
              "# command: rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- "
              "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
              f"{'kernel':60s} {'calls':>6s} {'avg_ms':>10s} {'min_ms':>10s} {'max_ms':>10s} {'pct':>6s}"]
@@ -123,15 +124,19 @@ def main():
                      f"{float(r['MinNs'])/1e6:10.4f} {float(r['MaxNs'])/1e6:10.4f} "
                      f"{float(r['Percentage']):6.2f}")
     chunk_avg = [float(r["AverageNs"]) / 1e6 for r in rows if CHUNK_TAG in r["Name"]]
-    # per dispatch: the timed steps are the last STEPS chunk-kernel launches
-    STEPS = 10
+    # per dispatch: bench.py launches the chunk kernel WARMUP + STEPS times
+    # for the headline workload (T=65536) first, then as often for each of the
+    # other two prefill workloads; the headline's timed steps are launches
+    # WARMUP .. WARMUP + STEPS - 1
+    WARMUP, STEPS = 2, 10
     ktrace = os.path.join(os.path.dirname(args.trace), "bench_kernel_trace.csv")
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
             for r in csv.DictReader(open(ktrace)) if CHUNK_TAG in r["Kernel_Name"]]
-    timed_avg = statistics.mean(durs[-STEPS:]) if len(durs) >= STEPS else None
+    timed = durs[WARMUP:WARMUP + STEPS]
+    timed_avg = statistics.mean(timed) if len(timed) == STEPS else None
     lines += ["", f"# chunk kernel per dispatch (ms): {' '.join(f'{d:.3f}' for d in durs)}",
-              f"# chunk kernel average over the {STEPS} timed steps: "
-              + (f"{timed_avg:.4f} ms" if timed_avg else "n/a")]
+              f"# chunk kernel average over the {STEPS} timed steps of T=65536 (launches "
+              f"{WARMUP + 1}..{WARMUP + STEPS}): " + (f"{timed_avg:.4f} ms" if timed_avg else "n/a")]
 
     # byte counters
     fetch = per_dispatch(args.fetch, "FETCH_SIZE")
@@ -164,7 +169,7 @@ def main():
         "traffic_bytes_per_launch": fb + wb,
         "algorithmic_bytes_per_launch": algo,
         "traffic_over_algorithmic": (fb + wb) / algo,
-        "kernel_trace_avg_ms": chunk_avg[0] if chunk_avg else None,
+        "kernel_trace_avg_ms_all_workloads": chunk_avg[0] if chunk_avg else None,
         "kernel_trace_timed_avg_ms": timed_avg,
     }
     lines += ["",
@@ -184,6 +189,19 @@ def main():
          bench.decode_bytes(256, 96, 128)),
         ("decode, 4 tokens (kda_decode_multi, B=256)", "decode_multi_kernelIDF16bLi128ELb0",
          bench.decode_multi_bytes(256, 4, 96, 128)),
+    ]
+    # the latent-attention decode step (256 sequences x 4096 cached latents,
+    # 96 heads, one split per sequence): each kernel against the bytes it must
+    # move, its split partials (m, l, U in fp32) included
+    B, H, L, R, Dh = 256, 96, 4096, 512, 128
+    partials = B * H * (R + 2) * 4
+    kinds += [
+        ("latent attn: absorb (q' = W_uk^T q)", "mla_absorb_kernel",
+         B * H * Dh * 2 + H * Dh * R * 2 + B * H * R * 2),
+        ("latent attn: attention over the cache", "mla_attn_kernel",
+         B * L * R * 2 + B * H * R * 2 + partials),
+        ("latent attn: combine (o = W_uv u, gate)", "mla_combine_kernel",
+         partials + H * Dh * R * 2 + 2 * B * H * Dh * 2),
     ]
     table = ["# HBM bytes per dispatch from rocprofv3 FETCH_SIZE and WRITE_SIZE (two runs of",
              "#   python3 bench.py --counters), scaled by the same counters on a copy kernel",
