@@ -6,6 +6,10 @@ kda_conv -> kda_chunk_prefill -> kda_gated_norm, inputs resident in HBM.
 ``value`` is prefill tokens/s.  The decode step (B = 256, 64 consecutive
 steps) is timed in the same run and reported as TB/s under ``decode``.
 
+The same run also times the other two prefill workloads, decode with K
+tokens per call, the latent-attention decode step, and the chunk kernel
+alone over one sequence of 2^20 tokens (the 1M-token regime).
+
 The roofline object describes the dominant kernel (the chunkwise recurrence):
 achieved = its algorithmic bytes per launch / its average launch duration,
 timed with HIP events on the stream it runs on.  ``cpu_baseline`` times the
@@ -155,6 +159,45 @@ def bench_mla(kda, synth, torch, stream, reps):
             "tflops_algorithmic": fl / (med * 1e-3) / 1e12,
             "mfma_frac": fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "tokens_per_s": B / (med * 1e-3)}
+
+
+def bench_chunk_1m(kda, torch, stream, H, D, C, steps):
+    """kda_chunk_prefill on one sequence of 2^20 tokens: q and k with unit
+    norm on average, v in [-1, 1], log-decay in [-5, 0], beta in (0.1, 0.9)."""
+    N = 1 << 20
+    HD = H * D
+    log(f"allocating the 1M-token chunk workload ({N} tokens, {H} heads)")
+    y_qkv = torch.empty((N, 3 * HD), dtype=torch.bfloat16, device="cuda")
+    y_qkv[:, :2 * HD].uniform_(-0.15, 0.15)
+    y_qkv[:, 2 * HD:].uniform_(-1.0, 1.0)
+    g = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda").uniform_(-5.0, 0.0)
+    beta = torch.empty((N, H), dtype=torch.bfloat16, device="cuda").uniform_(0.1, 0.9)
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+
+    def call():
+        kda.kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD, g,
+                              beta, o, 1, N, H, D, D, chunk=C, final_state=sT, stream=stream)
+
+    call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    finite = bool(torch.isfinite(sT).all())
+    nb = prefill_bytes(N, H, D, 1)["chunk"]
+    log(f"1M-token chunk kernel: {ms:.2f} ms, {N / ms / 1e3:.2f} M tokens/s")
+    del y_qkv, g, beta, o, sT
+    torch.cuda.empty_cache()
+    return {"workload": f"chunk_prefill_T{N}_H{H}_D{D}_bf16 (one sequence)", "tokens": N,
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
+            "achieved_GBs": nb / (ms * 1e-3) / 1e9,
+            "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "final_state_finite": finite}
 
 
 def cpu_baseline(inp, spec, T_s, H_s):
@@ -485,10 +528,18 @@ def main():
     if not args.no_decode:
         result["mla_decode"] = bench_mla(kda, synth, torch, stream, reps=max(args.steps, 10))
 
+
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_tokens, args.cpu_heads)
         log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
+    # the 1M-token regime: the chunk kernel alone over one sequence of
+    # 1,048,576 tokens at 96 x 128 (129 GB of device buffers, filled in place
+    # in bf16 with the value ranges of the workloads above)
+    del inp, x, w, g, beta, gate, nw, y_qkv, o, y
+    torch.cuda.empty_cache()
+    result["prefill_T1048576_chunk"] = bench_chunk_1m(kda, torch, stream, H, D, C,
+                                                      steps=max(args.steps // 3, 3))
     print(json.dumps(result), flush=True)
 
 

@@ -118,6 +118,10 @@ STRESS = {
     "long_carry": PrefillSpec("long_carry_T65536_H4_D128_bf16", H=4, D=128, dtype="bf16",
                               lengths=(65536,), g_lo=-2e-5, beta_mean=-6.0, beta_std=0.5,
                               s0_std=0.1, seed=2002),
+    # the 1M-token regime: the state carried across 65,536 chunks
+    "long_carry_1M": PrefillSpec("long_carry_T1048576_H2_D128_bf16", H=2, D=128, dtype="bf16",
+                                 lengths=(1048576,), g_lo=-2e-5, beta_mean=-6.0, beta_std=0.5,
+                                 s0_std=0.1, seed=2003),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}

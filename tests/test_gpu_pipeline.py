@@ -66,6 +66,13 @@ def test_stress_long_carry_all_heads():
     _run_config(synth.STRESS["long_carry"], heads=[0, 1, 2, 3])
 
 
+def test_stress_long_carry_1M_tokens():
+    """The 1M-token regime: one sequence of 1,048,576 tokens (65,536 chunks),
+    slow decay and small write strengths, every output and the final state
+    of both heads against the oracle."""
+    _run_config(synth.STRESS["long_carry_1M"], heads=[0, 1])
+
+
 def test_config4_decode_64_steps_sampled_pairs():
     spec = synth.CONFIGS[4]
     B, H, D, steps = spec.B, spec.H, spec.D, spec.steps
