@@ -12,13 +12,13 @@
 // (512 wide), so a score is q'_h . c_i and all heads read the same latent: one
 // pass over the cache serves every head.  The value up-projection is applied
 // after the softmax-weighted sum of latents, u_h = sum_i p_hi c_i, as
-// o_h = W_uv[h] u_h.  Three kernels:
-//  1. absorb: q' in bf16, scaled by scale * log2(e) (the softmax runs in
-//     base 2);
+// o_h = W_uv[h] u_h.  Three kernels, all on 16x16x32 bf16 MFMA:
+//  1. absorb: q' = q W_uk[h] in bf16, scaled by scale * log2(e) (the softmax
+//     runs in base 2);
 //  2. attention over a range of the cache, all heads at once, per
-//     (sequence, split): S = Q' C^T and U += P C on 16x16x32 MFMA with a
-//     running (online) softmax, partial m, l, U to the workspace;
-//  3. combine the splits, o = W_uv u, y = o * sigmoid(gate).
+//     (sequence, split): S^T = C Q'^T and U += P C with a running (online)
+//     softmax, partial m, l, U to the workspace;
+//  3. combine the splits, o = u W_uv[h]^T, y = o * sigmoid(gate).
 #include <hip/hip_runtime.h>
 
 #include "kda_device.hpp"
