@@ -251,3 +251,43 @@ def test_chunk16_repeatable():
         f(S0[s, h]))
     assert report("o", f(outs[0][0][t0:t1, h]), o_ref, TOL["bf16"]) <= TOL["bf16"]
     assert report("S_T", f(outs[0][1][s, h]), S_ref, TOL["bf16"]) <= TOL["bf16"]
+
+
+def test_chunk16_bitwise_under_concurrent_load():
+    """The slot hand-over must not depend on timing: the 16-token kernel at
+    96 heads gives bitwise the same outputs and final states when another
+    stream streams memory copies on the same GPU (which changes how its
+    waves are scheduled and how long their memory operations take) as when
+    it runs alone."""
+    H, D, N = 96, 128, 4096
+    HD = H * D
+    dt = torch.bfloat16
+    print("chunk16 under concurrent load: T=4096 H=96", flush=True)
+    qkv = torch.empty((N, 3 * HD), dtype=dt, device="cuda")
+    qkv[:, :HD] = _unit_rows((N, H, D), 50, dt).reshape(N, HD)
+    qkv[:, HD:2 * HD] = _unit_rows((N, H, D), 51, dt).reshape(N, HD)
+    qkv[:, 2 * HD:] = _randn((N, HD), 52, dt)
+    g = (-5.0 * torch.rand((N, H, D), generator=_gen(53), device="cuda")).to(dt)
+    beta = torch.sigmoid(torch.randn((N, H), generator=_gen(54), device="cuda")).to(dt)
+
+    def run(stream):
+        o = torch.empty((N, H, D), dtype=dt, device="cuda")
+        sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+        kda.kda_chunk_prefill(qkv[:, :HD], qkv[:, HD:2 * HD], qkv[:, 2 * HD:], 3 * HD, g, beta, o,
+                              1, N, H, D, D, chunk=16, final_state=sT, stream=stream)
+        return o, sT
+
+    main = torch.cuda.current_stream()
+    o_ref, s_ref = run(main)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()   # default priority
+    for rep in range(4):
+        with torch.cuda.stream(side):
+            for _ in range(8):
+                dst.copy_(src)
+        o, sT = run(main)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"o differs under concurrent load (call {rep})"
+        assert torch.equal(sT, s_ref), f"final state differs under concurrent load (call {rep})"
