@@ -245,3 +245,39 @@ def mla_decode(q, w_uk, w_uv, cache, lengths, gate, scale=None):
             o = p @ v
             y[b, h] = o * sigmoid(np.asarray(gate[b, h], np.float64))
     return y
+
+
+# ------------------------------------------------------------------ MXFP8 inputs
+# The pages quantise activations to MXFP8 ("Inside Kimi K3", model at a
+# glance: MXFP4 weights, MXFP8 activations from SFT onward) without spelling
+# the format out.  Read as the OCP microscaling format: 8-bit E4M3 elements
+# sharing one power-of-two E8M0 scale per block of 32 consecutive values.
+
+def e4m3_value(code):
+    """Value of an E4M3 byte: sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 encodes subnormals m/8 * 2^-6; no infinities; the two
+    codes with all exponent and mantissa bits set are NaN."""
+    code = np.asarray(code, dtype=np.int64)
+    s = (code >> 7) & 1
+    e = (code >> 3) & 15
+    m = code & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def e8m0_value(code):
+    """Value of an E8M0 scale byte: 2^(code - 127); code 255 is NaN."""
+    code = np.asarray(code, dtype=np.int64)
+    return np.where(code == 255, np.nan, 2.0 ** (code.astype(np.float64) - 127))
+
+
+def mxfp8_decode(codes, scales, block=32):
+    """MXFP8 tensor to fp64: codes [..., C] (E4M3 bytes), scales [..., C/block]
+    (E8M0 bytes, one per block of `block` consecutive values of the last
+    axis); value = e4m3(code) * e8m0(scale of its block)."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    C = codes.shape[-1]
+    assert C % block == 0 and scales.shape[-1] == C // block
+    return e4m3_value(codes) * np.repeat(e8m0_value(scales), block, axis=-1)

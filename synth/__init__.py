@@ -245,3 +245,24 @@ def mla_inputs(spec: MlaSpec, device="cpu", lengths=None):
         lengths=torch.tensor(lengths, dtype=torch.int32, device=device),
         lengths_list=list(lengths),
     )
+
+
+def mxfp8_encode(x: torch.Tensor, block: int = 32):
+    """Encode a tensor as MXFP8 along its last axis (OCP microscaling, E4M3
+    elements, one E8M0 scale per block of 32): the scale is the smallest power
+    of two that brings the block's largest magnitude to at most 448, E4M3's
+    largest finite value (so nothing saturates), and the scaled values are
+    rounded to E4M3.  Returns (codes uint8 [..., C], scales uint8
+    [..., C/32]).  Input preparation only: decoding is the oracle's and the
+    kernels' own."""
+    x = x.float()
+    C = x.shape[-1]
+    assert C % block == 0
+    xb = x.reshape(*x.shape[:-1], C // block, block)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax.clamp_min(2.0 ** -126) / 448.0)),
+                    torch.full_like(amax, -127.0)).clamp(-127.0, 127.0)
+    y = (xb / torch.exp2(e).unsqueeze(-1)).clamp(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(x.shape)
+    scales = (e + 127.0).to(torch.uint8)
+    return codes, scales
