@@ -6,9 +6,11 @@ kda_conv -> kda_chunk_prefill -> kda_gated_norm, inputs resident in HBM.
 ``value`` is prefill tokens/s.  The decode step (B = 256, 64 consecutive
 steps) is timed in the same run and reported as TB/s under ``decode``.
 
-The same run also times the other two prefill workloads, decode with K
-tokens per call, the latent-attention decode step, and the chunk kernel
-alone over one sequence of 2^20 tokens (the 1M-token regime).
+The same run also times the chunk kernel on MXFP8 inputs (the same
+activations encoded to E4M3 codes with E8M0 block scales), the other two
+prefill workloads, decode with K tokens per call, the latent-attention decode
+step, and the chunk kernel alone over one sequence of 2^20 tokens (the
+1M-token regime).
 
 The roofline object describes the dominant kernel (the chunkwise recurrence):
 achieved = its algorithmic bytes per launch / its average launch duration,
@@ -71,6 +73,17 @@ def prefill_bytes(N, H, D, n_seqs, es=2):
     conv = 2 * N * P * es               # x in, y out
     norm = 3 * N * H * D * es           # o, gate in, y out
     return dict(conv=conv, chunk=chunk, norm=norm)
+
+
+def mxfp8_chunk_bytes(N, H, D, n_seqs):
+    """Algorithmic HBM bytes of one kda_chunk_prefill_mxfp8 launch: q, k, v, g
+    as one-byte codes plus one scale byte per 32 values, beta and o in bf16,
+    the final state in fp32."""
+    return (4 * N * H * D              # q, k, v, g codes
+            + 4 * N * H * (D // 32)    # their block scales
+            + N * H * 2                # beta
+            + N * H * D * 2            # o
+            + n_seqs * H * D * D * 4)  # final state
 
 
 def chunk_flops(N, H, D, C=16):
@@ -200,6 +213,46 @@ def bench_chunk_1m(kda, torch, stream, H, D, C, steps):
             "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "final_state_finite": finite}
 
 
+def bench_chunk_mxfp8(kda, synth, torch, stream, y_qkv, g, beta, H, D, steps, warmup):
+    """kda_chunk_prefill_mxfp8 on the prefill workload's own activations (the
+    conv output q, k, v and the log-decay g), encoded to MXFP8 outside the
+    timed region; one sequence, timed with HIP events on the launch stream."""
+    N, HD = y_qkv.shape[0], H * D
+    codes, sc = synth.mxfp8_encode(y_qkv)
+    qs, ks, vs = (sc[:, i * H * (D // 32):(i + 1) * H * (D // 32)].contiguous()
+                  for i in range(3))
+    gc, gs = synth.mxfp8_encode(g)
+    gc, gs = gc.contiguous(), gs.contiguous()
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+
+    def call():
+        kda.kda_chunk_prefill_mxfp8(codes[:, :HD], qs, codes[:, HD:2 * HD], ks, codes[:, 2 * HD:],
+                                    vs, 3 * HD, gc, gs, beta, o, 1, N, H, final_state=sT,
+                                    stream=stream)
+
+    for _ in range(warmup):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    nb = mxfp8_chunk_bytes(N, H, D, 1)
+    log(f"MXFP8 chunk kernel: {ms:.3f} ms, {N / ms / 1e3:.2f} M tokens/s, "
+        f"{nb / ms / 1e6:.0f} GB/s")
+    del codes, sc, qs, ks, vs, gc, gs, o, sT
+    return {"workload": f"chunk_prefill_T{N}_H{H}_D{D}_mxfp8 (q, k, v, g as E4M3 codes with one "
+                        f"E8M0 scale per 32 values; beta, o bf16)",
+            "tokens": N, "steps": steps, "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
+            "bytes_per_call": nb, "achieved_GBs": nb / (ms * 1e-3) / 1e9,
+            "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(inp, spec, T_s, H_s):
     """Oracle on the first T_s tokens of the first H_s heads (all its threads)."""
     import numpy as np
@@ -298,6 +351,8 @@ def main():
                                   g, beta, o, 1, N, H, D, D, chunk=C, final_state=sT,
                                   stream=stream)
         kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
+        # the MXFP8 chunk kernel on the same activations, three launches
+        bench_chunk_mxfp8(kda, synth, torch, stream, y_qkv, g, beta, H, D, steps=3, warmup=0)
         # the decode kernels: three one-token steps, two calls of four tokens
         dspec = synth.CONFIGS[4]
         Bd, Hd, Dd = dspec.B, dspec.H, dspec.D
@@ -321,8 +376,9 @@ def main():
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("counter run done: conv, 3 chunk launches, norm, 3 decode steps, 2 four-token "
-            "decode calls, 6 latent-attention decode steps, 3 copies of 2 GiB")
+        log("counter run done: conv, 3 chunk launches, norm, 3 MXFP8 chunk launches, 3 decode "
+            "steps, 2 four-token decode calls, 6 latent-attention decode steps, 3 copies of "
+            "2 GiB")
         return
 
     for _ in range(args.warmup):
@@ -374,6 +430,9 @@ def main():
         "kernels_ms": k_ms,
         "pipeline_gbs": sum(nbytes.values()) / (ms_step * 1e-3) / 1e9,
     }
+
+    result["prefill_T65536_chunk_mxfp8"] = bench_chunk_mxfp8(
+        kda, synth, torch, stream, y_qkv, g, beta, H, D, args.steps, args.warmup)
 
     # the other two prefill workloads, timed the same way (informative: the
     # headline value is the workload above)

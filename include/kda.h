@@ -127,6 +127,36 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_t
                       int32_t dtype, hipStream_t s);
 
 /*
+ * kda_chunk_prefill_mxfp8 -- kda_chunk_prefill (16-token chunks, fp32
+ * state) with q, k, v and g given as MXFP8 activations.  ("Inside Kimi K3",
+ * model at a glance: activations quantised to MXFP8; read as the OCP
+ * microscaling format.)  Each tensor is a byte array of E4M3 codes (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+ * S.1111.111 = NaN) and a byte array of E8M0 scales, one per 32 consecutive
+ * channels: value = e4m3(code) * 2^(scale - 127), scale 255 = NaN.
+ *
+ *   q, k, v      [B*T, *] rows of H*128 codes at token stride
+ *                qkv_token_stride bytes (a multiple of 16, >= H*128)
+ *   q_scale, k_scale, v_scale, g_scale
+ *                [B*T, H, 4] scale bytes, contiguous
+ *   g            [B*T, H, 128] codes of the log-decay (clamped to [-5, 0]
+ *                after decoding, as in kda_chunk_prefill)
+ *   beta         [B*T, H] bf16; o [B*T, H, 128] bf16
+ *   initial_state, final_state, cu_seqlens, num_seqs, B, T: as in
+ *                kda_chunk_prefill (fp32 states, may alias)
+ * DK = DV = 128 only (others: KDA_ERR_UNSUPPORTED).  Code pointers, beta,
+ * o and the states must be 16-byte aligned; scale pointers need no
+ * alignment.  o must not overlap any input.
+ */
+int kda_chunk_prefill_mxfp8(const void* q, const void* q_scale, const void* k,
+                            const void* k_scale, const void* v, const void* v_scale,
+                            int64_t qkv_token_stride, const void* g, const void* g_scale,
+                            const void* beta, void* o, const float* initial_state,
+                            float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t B, int32_t T, int32_t H, int32_t DK, int32_t DV,
+                            hipStream_t s);
+
+/*
  * kda_decode_step -- one new token for each of B sequences: the conv window
  * [conv_state (3 values), x_t] per channel, SiLU, L2 of q and k, then one
  * gated-delta-rule step.  ("Inside Kimi K3", KDA short-convolution diagram,

@@ -13,7 +13,8 @@ import torch
 
 __all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
            "kda_decode_step", "kda_decode_multi", "kda_gated_norm", "kda_prefill",
-           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "KDA_F32", "KDA_BF16"]
+           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_chunk_prefill_mxfp8", "KDA_F32",
+           "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,12 +47,14 @@ def lib():
         L.kda_gated_norm.argtypes = [vp, vp, vp, vp, i64, i32, i32, f, i32, vp]
         L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        i32, f, vp]
+        L.kda_chunk_prefill_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
+                                              vp, i32, i32, i32, i32, i32, i32, vp]
         L.kda_mla_decode_workspace_bytes.argtypes = [i32, i32, i32]
         L.kda_mla_decode_workspace_bytes.restype = i64
         L.kda_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                      i32, f, i32, vp]
         for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
-                     "kda_decode_multi", "kda_mla_decode"):
+                     "kda_decode_multi", "kda_mla_decode", "kda_chunk_prefill_mxfp8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -138,6 +141,35 @@ def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, ch
                                    _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
                                    _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, T, H, DK,
                                    DV, chunk, _dtype(g), _stream(stream)))
+
+
+def kda_chunk_prefill_mxfp8(q, q_scale, k, k_scale, v, v_scale, qkv_token_stride, g, g_scale,
+                            beta, o, B, T, H, DK=128, DV=128, initial_state=None,
+                            final_state=None, cu_seqlens=None, num_seqs=0, stream=None):
+    """Chunkwise gated delta rule on MXFP8 q, k, v and g (see kda_chunk_prefill_mxfp8 in kda.h).
+
+    q, k, v are uint8 E4M3 codes (views into one [N, stride] byte tensor are
+    allowed; the token stride is in bytes); the *_scale tensors hold one E8M0
+    byte per 32 values; beta and o are bfloat16.
+    """
+    for t in (q, k, v, q_scale, k_scale, v_scale, g_scale):
+        if t.dtype != torch.uint8 or not t.is_cuda:
+            raise TypeError("codes and scales must be uint8 GPU tensors")
+    if g.dtype != torch.uint8:
+        raise TypeError("g must be uint8 E4M3 codes")
+    _same_dtype(beta, o)
+    if beta.dtype != torch.bfloat16:
+        raise TypeError("beta and o must be bfloat16")
+    _f32(initial_state, final_state)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check("kda_chunk_prefill_mxfp8",
+           lib().kda_chunk_prefill_mxfp8(q.data_ptr(), _ptr(q_scale), k.data_ptr(),
+                                         _ptr(k_scale), v.data_ptr(), _ptr(v_scale),
+                                         qkv_token_stride, _ptr(g), _ptr(g_scale), _ptr(beta),
+                                         _ptr(o), _ptr(initial_state), _ptr(final_state),
+                                         _ptr(cu_seqlens), num_seqs, B, T, H, DK, DV,
+                                         _stream(stream)))
 
 
 def kda_decode_step(x, w, conv_state, g, beta, state, o, B, H, D, l2_eps=1e-6, stream=None):

@@ -156,6 +156,60 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_t
                       fn);
 }
 
+int kda_chunk_prefill_mxfp8(const void* q, const void* q_scale, const void* k,
+                            const void* k_scale, const void* v, const void* v_scale,
+                            int64_t qkv_token_stride, const void* g, const void* g_scale,
+                            const void* beta, void* o, const float* initial_state,
+                            float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                            int32_t B, int32_t T, int32_t H, int32_t DK, int32_t DV,
+                            hipStream_t s) {
+    const char* fn = "kda_chunk_prefill_mxfp8";
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (DK != 128 || DV != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: DK and DV must be 128 (got %d, %d)", fn, DK, DV);
+    if (q == nullptr || k == nullptr || v == nullptr || g == nullptr || q_scale == nullptr ||
+        k_scale == nullptr || v_scale == nullptr || g_scale == nullptr || beta == nullptr ||
+        o == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: codes, scales, beta and o must be non-null", fn);
+    const int64_t row = (int64_t)H * 128;
+    if (qkv_token_stride < row || qkv_token_stride % 16 != 0)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "%s: qkv_token_stride must be >= H*128 and a multiple of 16 (got %lld)", fn,
+                    (long long)qkv_token_stride);
+    int ns;
+    int64_t N;
+    if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+        !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state))
+        return fail(KDA_ERR_INVALID_ARG,
+                    "%s: code, beta, o and state pointers must be 16-byte aligned", fn);
+    if ((int64_t)ns * H * 2 > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", fn);
+    const int64_t qkv_bytes = N > 0 ? (N - 1) * qkv_token_stride + row : 0;
+    const int64_t sc_bytes = N * H * 4;
+    const int64_t o_bytes = N * H * 128 * 2;
+    if (overlap(o, o_bytes, q, qkv_bytes) || overlap(o, o_bytes, k, qkv_bytes) ||
+        overlap(o, o_bytes, v, qkv_bytes) || overlap(o, o_bytes, g, N * H * 128) ||
+        overlap(o, o_bytes, q_scale, sc_bytes) || overlap(o, o_bytes, k_scale, sc_bytes) ||
+        overlap(o, o_bytes, v_scale, sc_bytes) || overlap(o, o_bytes, g_scale, sc_bytes) ||
+        overlap(o, o_bytes, beta, N * H * 2))
+        return fail(KDA_ERR_INVALID_ARG, "%s: o must not overlap an input", fn);
+    const int64_t st_bytes = (int64_t)ns * H * 128 * 128 * 4;
+    if (final_state != nullptr) {
+        if ((const void*)final_state != (const void*)initial_state &&
+            overlap(final_state, st_bytes, initial_state, st_bytes))
+            return fail(KDA_ERR_INVALID_ARG, "%s: final_state partially overlaps initial_state", fn);
+        if (overlap(final_state, st_bytes, o, o_bytes))
+            return fail(KDA_ERR_INVALID_ARG, "%s: final_state overlaps o", fn);
+    }
+    if (ns == 0) return ok();
+    return hip_status(kda::launch_chunk_pipe_mxfp8(q, q_scale, k, k_scale, v, v_scale,
+                                                   qkv_token_stride, g, g_scale, beta, o,
+                                                   initial_state, final_state, cu_seqlens, ns, T,
+                                                   H, s),
+                      fn);
+}
+
 int kda_decode_step(const void* x, const float* w, void* conv_state, const void* g,
                     const void* beta, float* state, void* o, int32_t B, int32_t H, int32_t D,
                     int32_t dtype, float l2_eps, hipStream_t s) {

@@ -302,13 +302,45 @@ __device__ __forceinline__ bool wait_at_least(int* f, int target, int* stop) {
     return true;
 }
 
-template <int DK, int DVS, int THREADS = PipeCfg<DK, DVS>::THREADS>
+// Element type of q, k, v and g: bf16, or MXFP8 (E4M3 codes, with one E8M0
+// scale byte per 32 consecutive channels in separate [tokens, H, D/32]
+// tensors).
+template <bool MX> struct PipeIn { using type = __bf16; };
+template <> struct PipeIn<true> { using type = uint8_t; };
+
+// lane n of the lane's 16-lane row, for a token index known after unrolling
+__device__ __forceinline__ float row_bcast_t(float x, int t) {
+    switch (t) {
+        case 0: return row_bcast<0>(x);   case 1: return row_bcast<1>(x);
+        case 2: return row_bcast<2>(x);   case 3: return row_bcast<3>(x);
+        case 4: return row_bcast<4>(x);   case 5: return row_bcast<5>(x);
+        case 6: return row_bcast<6>(x);   case 7: return row_bcast<7>(x);
+        case 8: return row_bcast<8>(x);   case 9: return row_bcast<9>(x);
+        case 10: return row_bcast<10>(x); case 11: return row_bcast<11>(x);
+        case 12: return row_bcast<12>(x); case 13: return row_bcast<13>(x);
+        case 14: return row_bcast<14>(x); default: return row_bcast<15>(x);
+    }
+}
+
+// E8M0 scale byte to its value 2^(s - 127) (code 0: 2^-127, code 255: NaN)
+__device__ __forceinline__ float e8m0_scale(uint32_t s) {
+    const uint32_t bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : s << 23);
+    return __builtin_bit_cast(float, bits);
+}
+
+template <int DK, int DVS, bool MX = false, int THREADS = PipeCfg<DK, DVS>::THREADS>
 __global__ void __launch_bounds__(THREADS)
-chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                  const __bf16* __restrict__ v, int64_t stride, const __bf16* __restrict__ g,
+chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
+                  const typename PipeIn<MX>::type* __restrict__ k,
+                  const typename PipeIn<MX>::type* __restrict__ v, int64_t stride,
+                  const typename PipeIn<MX>::type* __restrict__ g,
                   const __bf16* __restrict__ beta, __bf16* __restrict__ o, const float* s0,
                   float* sT, const int32_t* __restrict__ cu, int num_seqs, int T_len, int H,
-                  int DV, int nsplit) {
+                  int DV, int nsplit, const uint8_t* __restrict__ qsc,
+                  const uint8_t* __restrict__ ksc, const uint8_t* __restrict__ vsc,
+                  const uint8_t* __restrict__ gsc) {
+    static_assert(!MX || DK == 128, "MXFP8 inputs: two channels per producer lane");
+    constexpr int ES = MX ? 1 : 2;   // bytes per q, k, v, g element
     using Cfg = PipeCfg<DK, DVS>;
     constexpr int NC = Cfg::NC, NKS = Cfg::NKS, NKT = Cfg::NKT;
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
@@ -368,13 +400,20 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         uint32_t rg[16], rk[16], rq[16];   // CPL bf16 channels per word
         // V slice of the chunk: lane holds token lane/4, columns 16 (lane%4) .. +15
         bf16x8 rv[2];
+        // MXFP8: the V codes (16 per lane) and their scale byte; the scale
+        // bytes of g, k, q for the chunk's 16 tokens x 4 channel blocks, lane
+        // (block b, token t) holding (t, b) -- row b of lanes serves block b
+        u32x4 rvm;
+        uint32_t rvs, rsg, rsk, rsq;
         // beta of token lr as a zero-extended 32-bit word (16-bit values would
         // be packed in pairs right after the loads, which makes the wave wait)
         uint32_t rbl;
-        const int g_row = H * DK * 2, kv_row = (int)(stride * 2), b_row = H * 2;
+        const int g_row = H * DK * ES, kv_row = (int)(stride * ES), b_row = H * 2;
+        const int sc_row = H * (DK / 32);   // scale bytes per token
         const int vt = lane >> 2, vc = 16 * (lane & 3);
         auto load_word = [](rsrc_t r, int off) -> uint32_t {
-            if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+            if constexpr (MX) return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+            else if constexpr (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
             else return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
         };
         // Loads of chunk ci (g, k, q, beta; V separately).  Past the last chunk
@@ -394,9 +433,17 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                rg[t] = load_word(r_g, t * g_row + c0 * 2);
-                rk[t] = load_word(r_k, t * kv_row + c0 * 2);
-                rq[t] = load_word(r_q, t * kv_row + c0 * 2);
+                rg[t] = load_word(r_g, t * g_row + c0 * ES);
+                rk[t] = load_word(r_k, t * kv_row + c0 * ES);
+                rq[t] = load_word(r_q, t * kv_row + c0 * ES);
+            }
+            if constexpr (MX) {
+                const int64_t sb = (t0 * H + head) * (DK / 32);
+                const uint32_t sbytes = (uint32_t)(valid * sc_row);
+                const int soff = lr * sc_row + lq;
+                rsg = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(make_rsrc(gsc + sb, sbytes), soff, 0, 0);
+                rsk = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(make_rsrc(ksc + sb, sbytes), soff, 0, 0);
+                rsq = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(make_rsrc(qsc + sb, sbytes), soff, 0, 0);
             }
             const rsrc_t r_b = make_rsrc(beta + t0 * H + head, (uint32_t)(valid * b_row));
             rbl = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_b, lr * b_row, 0, 0);
@@ -405,8 +452,16 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             int64_t t0;
             const int valid = chunk_rows(ci, t0);
             const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
-            rv[0] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2);
-            rv[1] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2 + 16);
+            if constexpr (MX) {
+                rvm = __builtin_amdgcn_raw_buffer_load_b128(r_v, vt * kv_row + vc, 0, 0);
+                const int vrow = H * (DV / 32);
+                rvs = (uint32_t)(uint8_t)__builtin_amdgcn_raw_buffer_load_b8(
+                    make_rsrc(vsc + (t0 * H + head) * (DV / 32), (uint32_t)(valid * vrow)),
+                    vt * vrow + (n0 + vc) / 32, 0, 0);
+            } else {
+                rv[0] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2);
+                rv[1] = BufLoad<__bf16, 8>::load(r_v, vt * kv_row + vc * 2 + 16);
+            }
         };
         // channel j of a word as fp32 (bf16 is the top half of an fp32)
         auto chan = [](uint32_t w, int j) -> float {
@@ -446,15 +501,28 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             // E_t = e^{-G_t} = e^{-G_15} a_{t+1} .. a_15 (backward)
             float a[CPL][16], F[CPL];
             uint32_t wkt[16], wqt[16], wki[16];   // packed bf16 tile words per token
+            // MXFP8: the block scales of g, k, q (one per lane: token lr of
+            // block lq); value j of token t is then one scaled conversion of
+            // the two codes with the scale broadcast from lane t of the row
+            float fsg = 0.f, fsk = 0.f, fsq = 0.f;
+            if constexpr (MX) {
+                fsg = e8m0_scale(rsg);
+                fsk = e8m0_scale(rsk);
+                fsq = e8m0_scale(rsq);
+            }
+            auto val = [&](uint32_t w, float fs, int t, int j) -> float {
+                if constexpr (MX) return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, row_bcast_t(fs, t), false)[j];
+                else return chan(w, j);
+            };
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 float kt[CPL], qt[CPL];
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
-                    a[j][t] = fast_exp2(clamp_log_decay(chan(rg[t], j)) * kLog2e);
+                    a[j][t] = fast_exp2(clamp_log_decay(val(rg[t], fsg, t, j)) * kLog2e);
                     F[j] = t == 0 ? a[j][0] : F[j] * a[j][t];
-                    kt[j] = -(chan(rk[t], j) * F[j]);   // stored negated: -K e^G
-                    qt[j] = chan(rq[t], j) * F[j];
+                    kt[j] = -(val(rk[t], fsk, t, j) * F[j]);   // stored negated: -K e^G
+                    qt[j] = val(rq[t], fsq, t, j) * F[j];
                 }
                 wkt[t] = pack(kt);
                 wqt[t] = pack(qt);
@@ -468,7 +536,7 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     if (t < 15) E[j] *= a[j][t + 1];
-                    ki[j] = chan(rk[t], j) * E[j];
+                    ki[j] = val(rk[t], fsk, t, j) * E[j];
                 }
                 wki[t] = pack(ki);
             }
@@ -507,6 +575,21 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                 float* gp = reinterpret_cast<float*>(slot + Cfg::O_GM) + ((qq * 16 + 2 * kt + (i >> 1)) * 2 + (i & 1));
                 if constexpr (CPL == 2) *reinterpret_cast<floatx2*>(gp) = floatx2{F[0], F[1]};
                 else *gp = F[0];
+            }
+            if constexpr (MX) {
+                // the 16 V codes of this lane to bf16 (exact: E4M3 times a
+                // power of two fits bf16)
+                const float fv = e8m0_scale(rvs);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const floatx2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rvm[2 * h], fv, false);
+                    const floatx2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rvm[2 * h], fv, true);
+                    const floatx2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rvm[2 * h + 1], fv, false);
+                    const floatx2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rvm[2 * h + 1], fv, true);
+                    const bf16x2 b0 = __builtin_convertvector(p0, bf16x2), b1 = __builtin_convertvector(p1, bf16x2);
+                    const bf16x2 b2 = __builtin_convertvector(p2, bf16x2), b3 = __builtin_convertvector(p3, bf16x2);
+                    rv[h] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+                }
             }
             *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
             *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
@@ -740,18 +823,21 @@ chunk_pipe_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
 }
 
-template <int DK, int DVS>
+template <int DK, int DVS, bool MX>
 hipError_t launch_pipe_t(const void* q, const void* k, const void* v, int64_t stride,
                          const void* g, const void* beta, void* o, const float* s0, float* sT,
                          const int32_t* cu, int num_seqs, int T_len, int H, int DV,
+                         const void* qsc, const void* ksc, const void* vsc, const void* gsc,
                          hipStream_t s) {
+    using TIn = typename PipeIn<MX>::type;
     const int nsplit = DV / DVS;
     const int64_t blocks = (int64_t)num_seqs * H * nsplit;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS>), dim3((unsigned)blocks),
-                       dim3(PipeCfg<DK, DVS>::THREADS), 0, s, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, stride, (const __bf16*)g, (const __bf16*)beta, (__bf16*)o,
-                       s0, sT, cu, num_seqs, T_len, H, DV, nsplit);
+    hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS, MX>), dim3((unsigned)blocks),
+                       dim3(PipeCfg<DK, DVS>::THREADS), 0, s, (const TIn*)q, (const TIn*)k,
+                       (const TIn*)v, stride, (const TIn*)g, (const __bf16*)beta, (__bf16*)o,
+                       s0, sT, cu, num_seqs, T_len, H, DV, nsplit, (const uint8_t*)qsc,
+                       (const uint8_t*)ksc, (const uint8_t*)vsc, (const uint8_t*)gsc);
     return hipGetLastError();
 }
 
@@ -762,8 +848,19 @@ hipError_t launch_chunk_pipe(const void* q, const void* k, const void* v, int64_
                              float* sT, const int32_t* cu, int num_seqs, int T, int H, int DK,
                              int DV, hipStream_t s) {
     if (DK == 128)
-        return launch_pipe_t<128, 64>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H, DV, s);
-    return launch_pipe_t<64, 64>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H, DV, s);
+        return launch_pipe_t<128, 64, false>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T,
+                                             H, DV, nullptr, nullptr, nullptr, nullptr, s);
+    return launch_pipe_t<64, 64, false>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
+                                        DV, nullptr, nullptr, nullptr, nullptr, s);
+}
+
+hipError_t launch_chunk_pipe_mxfp8(const void* q, const void* qsc, const void* k,
+                                   const void* ksc, const void* v, const void* vsc,
+                                   int64_t stride, const void* g, const void* gsc,
+                                   const void* beta, void* o, const float* s0, float* sT,
+                                   const int32_t* cu, int num_seqs, int T, int H, hipStream_t s) {
+    return launch_pipe_t<128, 64, true>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
+                                        128, qsc, ksc, vsc, gsc, s);
 }
 
 }  // namespace kda

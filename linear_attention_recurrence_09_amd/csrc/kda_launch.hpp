@@ -40,6 +40,14 @@ hipError_t launch_chunk_pipe(const void* q, const void* k, const void* v, int64_
                              float* sT, const int32_t* cu, int num_seqs, int T, int H, int DK,
                              int DV, hipStream_t s);
 
+// MXFP8 q, k, v, g (E4M3 codes; E8M0 scales [tokens, H, 4] per tensor), bf16
+// beta and o, DK = DV = 128, 16-token chunks (kda_chunk_pipe.hip).
+hipError_t launch_chunk_pipe_mxfp8(const void* q, const void* qsc, const void* k,
+                                   const void* ksc, const void* v, const void* vsc,
+                                   int64_t stride, const void* g, const void* gsc,
+                                   const void* beta, void* o, const float* s0, float* sT,
+                                   const int32_t* cu, int num_seqs, int T, int H, hipStream_t s);
+
 hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, const void* v,
                         int64_t stride, const void* g, const void* beta, void* o,
                         const float* s0, float* sT, const int32_t* cu, int num_seqs, int T,

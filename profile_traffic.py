@@ -30,7 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 COPY_BYTES = 2 * 1024 ** 3
-CHUNK_TAG = "chunk_pipe_kernel"
+# mangled names as rocprofv3 -T prints them: the bf16 and the MXFP8
+# instantiation of the 16-token chunk kernel (template flag b0 / b1)
+CHUNK_TAG = "chunk_pipe_kernelILi128ELi64ELb0E"
+MX_TAG = "chunk_pipe_kernelILi128ELi64ELb1E"
 COPY_TAG = "vectorized_elementwise_kernel"
 
 
@@ -184,6 +187,8 @@ def main():
     kinds = [
         ("conv (kda_conv, T=65536)", "conv_kernel", pb["conv"]),
         ("chunk (kda_chunk_prefill, chunk 16, T=65536)", CHUNK_TAG, pb["chunk"]),
+        ("chunk MXFP8 (kda_chunk_prefill_mxfp8, T=65536)", MX_TAG,
+         bench.mxfp8_chunk_bytes(65536, 96, 128, 1)),
         ("gated norm (kda_gated_norm, T=65536)", "gated_norm_kernel", pb["norm"]),
         ("decode, 1 token (kda_decode_step, B=256)", "decode_multi_kernelIDF16bLi128ELb1",
          bench.decode_bytes(256, 96, 128)),

@@ -30,7 +30,7 @@ def L():
 
 
 def test_header_declares_the_calls():
-    assert declared() == ["kda_chunk_prefill", "kda_conv", "kda_decode_multi", "kda_decode_step",
+    assert declared() == ["kda_chunk_prefill", "kda_chunk_prefill_mxfp8", "kda_conv", "kda_decode_multi", "kda_decode_step",
                           "kda_gated_norm", "kda_last_error", "kda_mla_decode",
                           "kda_mla_decode_workspace_bytes", "kda_version"]
 
@@ -86,6 +86,32 @@ def test_chunk_argument_checks(L):
     assert chunk(L, s0=A + 256 * MB, sT=A + 256 * MB + 16) == INVALID
     assert chunk(L, B=0) == OK
     assert "kda_chunk_prefill" in kda.kda_last_error()
+
+
+def chunk_mx(L, q=A, qs=A + 32 * MB, k=A + 128, ks=A + 33 * MB, v=A + 256, vs=A + 34 * MB,
+             stride=3 * 2 * 128, g=A + 64 * MB, gs=A + 35 * MB, b=A + 96 * MB, o=A + 128 * MB,
+             s0=None, sT=None, cu=None, ns=0, B=1, T=8, H=2, DK=128, DV=128):
+    return L.kda_chunk_prefill_mxfp8(q, qs, k, ks, v, vs, stride, g, gs, b, o, s0, sT, cu, ns, B,
+                                     T, H, DK, DV, None)
+
+
+def test_chunk_mxfp8_argument_checks(L):
+    assert chunk_mx(L, q=None) == INVALID
+    for name in ("qs", "ks", "vs", "gs"):
+        assert chunk_mx(L, **{name: None}) == INVALID        # every block scale is required
+    assert chunk_mx(L, DK=64) == UNSUPPORTED
+    assert chunk_mx(L, DV=64) == UNSUPPORTED
+    assert chunk_mx(L, H=0) == INVALID
+    assert chunk_mx(L, stride=200) == INVALID                # below H*128 bytes
+    assert chunk_mx(L, stride=264) == INVALID                # not a multiple of 16
+    assert chunk_mx(L, q=A + 8) == INVALID                   # misaligned codes
+    assert chunk_mx(L, o=A + 64) == INVALID                  # o overlaps the codes
+    assert chunk_mx(L, o=A + 34 * MB) == INVALID             # o overlaps v's scales
+    assert chunk_mx(L, o=A + 64 * MB + 512) == INVALID       # o overlaps g
+    assert chunk_mx(L, s0=A + 256 * MB, sT=A + 256 * MB + 16) == INVALID
+    assert chunk_mx(L, cu=A + 300 * MB, B=2) == INVALID      # varlen needs B == 1
+    assert chunk_mx(L, B=0) == OK
+    assert "kda_chunk_prefill_mxfp8" in kda.kda_last_error()
 
 
 def test_decode_and_norm_argument_checks(L):
