@@ -9,6 +9,9 @@ recurrence, used to pin it:
 * :func:`gated_delta_rule_bruteforce` -- the state after T steps written as a
   product of explicit dk x dk transition matrices (for tiny T).
 
+It also holds MXFP8 (OCP microscaling: E4M3 elements, one E8M0 scale per 32
+values) decoding and encoding, written from the format's definition.
+
 Pages cited:
   [CONV] "Inside Kimi K3" (lei.chat), KDA short-convolution diagram.
   [KDA]  "Inside Kimi K3" (lei.chat), Kimi Delta Attention one-head diagram.
@@ -281,3 +284,52 @@ def mxfp8_decode(codes, scales, block=32):
     C = codes.shape[-1]
     assert C % block == 0 and scales.shape[-1] == C // block
     return e4m3_value(codes) * np.repeat(e8m0_value(scales), block, axis=-1)
+
+
+# Non-negative finite E4M3 magnitudes by code (0x00 .. 0x7E), ascending.
+_E4M3_POS = e4m3_value(np.arange(127))
+
+
+def e8m0_exponent_for(amax):
+    """Block exponent of the MXFP8 encoding: the smallest integer e with
+    amax <= 448 * 2^e (448 is E4M3's largest finite value, so no element of
+    the block saturates), clamped to E8M0's range [-127, 127]; an all-zero
+    block takes -127.  With amax = f * 2^E, f in [0.5, 1) and 448 =
+    0.875 * 2^9, that is e = E - 9 when f <= 0.875 and E - 8 otherwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(amax)
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.where(amax > 0, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def e4m3_round(y):
+    """E4M3 code of y (|y| <= 448), rounded to the nearest representable
+    value, ties to the even code (the one whose lowest mantissa bit is 0).
+    The sign goes into bit 7; zero gives code 0."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    assert np.all(a <= 448.0), "scaled value outside E4M3's finite range"
+    hi = np.searchsorted(_E4M3_POS, a, side="left")        # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == _E4M3_POS[hi], hi, np.where(pick_hi, hi, lo))
+    return np.where((y < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def mxfp8_encode(x, block=32):
+    """MXFP8 encoding along the last axis: per block of `block` consecutive
+    values, the E8M0 scale byte e + 127 with e from :func:`e8m0_exponent_for`
+    of the block's largest magnitude, and each value's E4M3 code of x / 2^e
+    (exact division by a power of two, then round to nearest even).  Returns
+    (codes uint8 [..., C], scales uint8 [..., C/block])."""
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    assert C % block == 0
+    xb = x.reshape(*x.shape[:-1], C // block, block)
+    e = e8m0_exponent_for(np.abs(xb).max(axis=-1))
+    codes = e4m3_round(np.ldexp(xb, -e[..., None])).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
