@@ -6,8 +6,9 @@ kda_conv -> kda_chunk_prefill -> kda_gated_norm, inputs resident in HBM.
 ``value`` is prefill tokens/s.  The decode step (B = 256, 64 consecutive
 steps) is timed in the same run and reported as TB/s under ``decode``.
 
-The same run also times the chunk kernel on MXFP8 inputs (the same
-activations encoded to E4M3 codes with E8M0 block scales), the other two
+The same run also times the prefill step with MXFP8 activations between
+the kernels (E4M3 codes with E8M0 block scales: kda_conv_mxfp8 ->
+kda_chunk_prefill_mxfp8 -> kda_gated_norm), the other two
 prefill workloads, decode with K tokens per call, the latent-attention decode
 step, and the chunk kernel alone over one sequence of 2^20 tokens (the
 1M-token regime).
@@ -213,44 +214,67 @@ def bench_chunk_1m(kda, torch, stream, H, D, C, steps):
             "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "final_state_finite": finite}
 
 
-def bench_chunk_mxfp8(kda, synth, torch, stream, y_qkv, g, beta, H, D, steps, warmup):
-    """kda_chunk_prefill_mxfp8 on the prefill workload's own activations (the
-    conv output q, k, v and the log-decay g), encoded to MXFP8 outside the
-    timed region; one sequence, timed with HIP events on the launch stream."""
-    N, HD = y_qkv.shape[0], H * D
-    codes, sc = synth.mxfp8_encode(y_qkv)
-    qs, ks, vs = (sc[:, i * H * (D // 32):(i + 1) * H * (D // 32)].contiguous()
-                  for i in range(3))
+def mxfp8_conv_bytes(N, H, D):
+    """Algorithmic HBM bytes of one kda_conv_mxfp8 launch: bf16 x in, one
+    code byte per channel and one scale byte per 32 channels out."""
+    P = 3 * H * D
+    return 2 * N * P + N * P + N * P // 32
+
+
+def bench_mxfp8_prefill(kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D, steps, warmup):
+    """The prefill step with MXFP8 activations between the kernels:
+    kda_conv_mxfp8 -> kda_chunk_prefill_mxfp8 -> kda_gated_norm, on the same
+    inputs as the bf16 step; g is encoded to MXFP8 outside the timed region
+    (its producer is outside this path).  HIP events on the launch stream."""
+    N, HD = x.shape[0], H * D
+    P = 3 * HD
+    codes = torch.empty((N, P), dtype=torch.uint8, device="cuda")
+    sc = [torch.empty((N, H, D // 32), dtype=torch.uint8, device="cuda") for _ in range(3)]
     gc, gs = synth.mxfp8_encode(g)
     gc, gs = gc.contiguous(), gs.contiguous()
     o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(o)
     sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
 
-    def call():
-        kda.kda_chunk_prefill_mxfp8(codes[:, :HD], qs, codes[:, HD:2 * HD], ks, codes[:, 2 * HD:],
-                                    vs, 3 * HD, gc, gs, beta, o, 1, N, H, final_state=sT,
-                                    stream=stream)
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        kda.kda_conv_mxfp8(x, w, codes, *sc, 1, N, H, D, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        kda.kda_chunk_prefill_mxfp8(codes[:, :HD], sc[0], codes[:, HD:2 * HD], sc[1],
+                                    codes[:, 2 * HD:], sc[2], P, gc, gs, beta, o, 1, N, H,
+                                    final_state=sT, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
+        if ev:
+            ev[3].record(stream)
 
     for _ in range(warmup):
-        call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for e0, e1 in evs:
-        e0.record(stream)
-        call()
-        e1.record(stream)
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
     torch.cuda.synchronize()
-    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
-    nb = mxfp8_chunk_bytes(N, H, D, 1)
-    log(f"MXFP8 chunk kernel: {ms:.3f} ms, {N / ms / 1e3:.2f} M tokens/s, "
-        f"{nb / ms / 1e6:.0f} GB/s")
-    del codes, sc, qs, ks, vs, gc, gs, o, sT
-    return {"workload": f"chunk_prefill_T{N}_H{H}_D{D}_mxfp8 (q, k, v, g as E4M3 codes with one "
-                        f"E8M0 scale per 32 values; beta, o bf16)",
-            "tokens": N, "steps": steps, "ms_per_call": ms, "tokens_per_s": N / (ms * 1e-3),
-            "bytes_per_call": nb, "achieved_GBs": nb / (ms * 1e-3) / 1e9,
-            "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    km = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+          for j, n in enumerate(("conv", "chunk", "norm"))}
+    nb = {"conv": mxfp8_conv_bytes(N, H, D), "chunk": mxfp8_chunk_bytes(N, H, D, 1),
+          "norm": prefill_bytes(N, H, D, 1)["norm"]}
+    log(f"MXFP8 prefill: {ms_step:.3f} ms/step ({N / ms_step / 1e3:.2f} M tokens/s); "
+        f"kernels {km}")
+    del codes, sc, gc, gs, o, y, sT
+    return {"workload": f"prefill_T{N}_H{H}_D{D}_mxfp8: kda_conv_mxfp8 -> "
+                        f"kda_chunk_prefill_mxfp8 -> kda_gated_norm (q, k, v, g as E4M3 codes "
+                        f"with one E8M0 scale per 32 values; x, beta, gate, o, y bf16)",
+            "tokens": N, "steps": steps, "ms_per_step": ms_step,
+            "tokens_per_s": N / (ms_step * 1e-3), "kernels_ms": km,
+            "bytes_per_launch": nb,
+            "kernels_GBs": {k: nb[k] / (km[k] * 1e-3) / 1e9 for k in km},
+            "kernels_hbm_frac": {k: nb[k] / (km[k] * 1e-3) / 1e9 / HBM_PEAK_GBS for k in km}}
 
 
 def cpu_baseline(inp, spec, T_s, H_s):
@@ -351,8 +375,9 @@ def main():
                                   g, beta, o, 1, N, H, D, D, chunk=C, final_state=sT,
                                   stream=stream)
         kda.kda_gated_norm(o, gate, nw, y, N, H, D, stream=stream)
-        # the MXFP8 chunk kernel on the same activations, three launches
-        bench_chunk_mxfp8(kda, synth, torch, stream, y_qkv, g, beta, H, D, steps=3, warmup=0)
+        # the MXFP8 step on the same inputs, three times (conv, chunk, norm)
+        bench_mxfp8_prefill(kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D, steps=3,
+                            warmup=0)
         # the decode kernels: three one-token steps, two calls of four tokens
         dspec = synth.CONFIGS[4]
         Bd, Hd, Dd = dspec.B, dspec.H, dspec.D
@@ -376,7 +401,7 @@ def main():
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("counter run done: conv, 3 chunk launches, norm, 3 MXFP8 chunk launches, 3 decode "
+        log("counter run done: conv, 3 chunk launches, norm, 3 MXFP8 prefill steps, 3 decode "
             "steps, 2 four-token decode calls, 6 latent-attention decode steps, 3 copies of "
             "2 GiB")
         return
@@ -431,8 +456,8 @@ def main():
         "pipeline_gbs": sum(nbytes.values()) / (ms_step * 1e-3) / 1e9,
     }
 
-    result["prefill_T65536_chunk_mxfp8"] = bench_chunk_mxfp8(
-        kda, synth, torch, stream, y_qkv, g, beta, H, D, args.steps, args.warmup)
+    result["prefill_T65536_mxfp8"] = bench_mxfp8_prefill(
+        kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D, args.steps, args.warmup)
 
     # the other two prefill workloads, timed the same way (informative: the
     # headline value is the workload above)

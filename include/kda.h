@@ -93,6 +93,30 @@ int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
              int32_t T, int32_t H, int32_t D, int32_t dtype, float l2_eps, hipStream_t s);
 
 /*
+ * kda_conv_mxfp8 -- kda_conv on bf16 inputs with its output written as MXFP8
+ * activations (the OCP microscaling reading of "Inside Kimi K3", model at a
+ * glance; the code and scale formats are those of kda_chunk_prefill_mxfp8
+ * below), ready to be read in place by kda_chunk_prefill_mxfp8.
+ *
+ *   x, w, conv_state_in, conv_state_out, cu_seqlens, num_seqs, B, T, H, D,
+ *   l2_eps          as in kda_conv, with x and the states in bf16
+ *   y_codes         [B*T, 3*H*D] E4M3 codes of kda_conv's y (q | k | v)
+ *   q_scale, k_scale, v_scale
+ *                   [B*T, H, D/32] E8M0 scale bytes, one per block of 32
+ *                   consecutive channels of a head
+ * Per block, the scale exponent e is the smallest integer with
+ * max|y| <= 448 * 2^e (clamped to [-127, 127]; an all-zero block gets
+ * scale byte 0), and each code is y * 2^-e rounded to the nearest E4M3
+ * value, ties to even, from y in fp32.  D = 64 or 128.  x, y_codes and the
+ * states must be 16-byte aligned, the scale pointers D/32-byte aligned;
+ * y_codes and the scales must not overlap x or each other.
+ */
+int kda_conv_mxfp8(const void* x, const float* w, void* y_codes, void* q_scale, void* k_scale,
+                   void* v_scale, const void* conv_state_in, void* conv_state_out,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                   int32_t D, float l2_eps, hipStream_t s);
+
+/*
  * kda_chunk_prefill -- the gated delta rule over whole sequences, evaluated
  * chunkwise: parallel within a chunk of `chunk` tokens, recurrent across
  * chunks.  ("Inside Kimi K3", KDA one-head diagram; "Animated Kimi K3

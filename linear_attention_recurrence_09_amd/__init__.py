@@ -13,7 +13,8 @@ import torch
 
 __all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
            "kda_decode_step", "kda_decode_multi", "kda_gated_norm", "kda_prefill",
-           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_chunk_prefill_mxfp8", "KDA_F32",
+           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_chunk_prefill_mxfp8", "kda_conv_mxfp8",
+           "KDA_F32",
            "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
@@ -47,6 +48,8 @@ def lib():
         L.kda_gated_norm.argtypes = [vp, vp, vp, vp, i64, i32, i32, f, i32, vp]
         L.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        i32, f, vp]
+        L.kda_conv_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     f, vp]
         L.kda_chunk_prefill_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, vp, vp,
                                               vp, i32, i32, i32, i32, i32, i32, vp]
         L.kda_mla_decode_workspace_bytes.argtypes = [i32, i32, i32]
@@ -54,7 +57,8 @@ def lib():
         L.kda_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                      i32, f, i32, vp]
         for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
-                     "kda_decode_multi", "kda_mla_decode", "kda_chunk_prefill_mxfp8"):
+                     "kda_decode_multi", "kda_mla_decode", "kda_chunk_prefill_mxfp8",
+                     "kda_conv_mxfp8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -141,6 +145,25 @@ def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, ch
                                    _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
                                    _ptr(final_state), _ptr(cu_seqlens), num_seqs, B, T, H, DK,
                                    DV, chunk, _dtype(g), _stream(stream)))
+
+
+def kda_conv_mxfp8(x, w, y_codes, q_scale, k_scale, v_scale, B, T, H, D, conv_state_in=None,
+                   conv_state_out=None, cu_seqlens=None, num_seqs=0, l2_eps=1e-6, stream=None):
+    """kda_conv with MXFP8 output (see kda_conv_mxfp8 in kda.h): bf16 x and
+    states; uint8 E4M3 codes [N, 3*H*D] and E8M0 scales [N, H, D/32] out."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    _same_dtype(x, conv_state_in, conv_state_out)
+    _f32(w)
+    for t in (y_codes, q_scale, k_scale, v_scale):
+        if t.dtype != torch.uint8:
+            raise TypeError("codes and scales must be uint8")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    _check("kda_conv_mxfp8",
+           lib().kda_conv_mxfp8(_ptr(x), _ptr(w), _ptr(y_codes), _ptr(q_scale), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(conv_state_in), _ptr(conv_state_out),
+                                _ptr(cu_seqlens), num_seqs, B, T, H, D, l2_eps, _stream(stream)))
 
 
 def kda_chunk_prefill_mxfp8(q, q_scale, k, k_scale, v, v_scale, qkv_token_stride, g, g_scale,

@@ -105,6 +105,55 @@ int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
                       fn);
 }
 
+int kda_conv_mxfp8(const void* x, const float* w, void* y_codes, void* q_scale, void* k_scale,
+                   void* v_scale, const void* conv_state_in, void* conv_state_out,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                   int32_t D, float l2_eps, hipStream_t s) {
+    const char* fn = "kda_conv_mxfp8";
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(l2_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps must be > 0", fn);
+    if (x == nullptr || w == nullptr || y_codes == nullptr || q_scale == nullptr ||
+        k_scale == nullptr || v_scale == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, w, y_codes and the scales must be non-null", fn);
+    int ns;
+    int64_t N;
+    if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    const int64_t P = 3LL * H * D;
+    if (!aligned16(x) || !aligned16(y_codes) || !aligned16(conv_state_in) ||
+        !aligned16(conv_state_out))
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, y_codes and state pointers must be 16-byte aligned",
+                    fn);
+    const uintptr_t sal = (uintptr_t)(D / 32);   // a head's scale bytes are written together
+    if ((uintptr_t)q_scale % sal || (uintptr_t)k_scale % sal || (uintptr_t)v_scale % sal)
+        return fail(KDA_ERR_INVALID_ARG, "%s: scale pointers must be %d-byte aligned", fn, D / 32);
+    const int64_t xb = N * P * 2, cb = N * P, sb = N * H * (D / 32);
+    const void* outs[4] = {y_codes, q_scale, k_scale, v_scale};
+    const int64_t lens[4] = {cb, sb, sb, sb};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], lens[i], x, xb))
+            return fail(KDA_ERR_INVALID_ARG, "%s: outputs must not overlap x", fn);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], lens[i], outs[j], lens[j]))
+                return fail(KDA_ERR_INVALID_ARG, "%s: outputs must not overlap each other", fn);
+    }
+    const int64_t stb = (int64_t)ns * P * 3 * 2;
+    if (conv_state_out != nullptr) {
+        if (conv_state_out != conv_state_in && overlap(conv_state_in, stb, conv_state_out, stb))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out partially overlaps conv_state_in", fn);
+        if (overlap(conv_state_out, stb, x, xb))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out overlaps x", fn);
+        for (int i = 0; i < 4; ++i)
+            if (overlap(conv_state_out, stb, outs[i], lens[i]))
+                return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out overlaps an output", fn);
+    }
+    if (N == 0 && (conv_state_out == nullptr || ns == 0)) return ok();
+    return hip_status(kda::launch_conv_mxfp8(x, w, y_codes, q_scale, k_scale, v_scale,
+                                             conv_state_in, conv_state_out, cu_seqlens, ns, T, N,
+                                             H, D, l2_eps, s),
+                      fn);
+}
+
 int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_token_stride,
                       const void* g, const void* beta, void* o, const float* initial_state,
                       float* final_state, const int32_t* cu_seqlens, int32_t num_seqs,

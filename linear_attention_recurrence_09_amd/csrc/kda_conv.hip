@@ -14,6 +14,20 @@
 // in registers across groups, so weights and halo are loaded once per strip.
 // D/8 lanes of one head reduce the sum of squares with xor shuffles.  A block
 // covers 2048 channels; windows restart at every sequence start.
+//
+// MXFP8 output (OCP microscaling: E4M3 elements, one E8M0 scale per 32
+// consecutive channels): the 4 lanes of a 32-channel block exchange their
+// largest magnitude (two xor shuffles, issued beside the L2 sum's, on the
+// values before normalisation: scaling by the positive L2 factor and
+// rounding are monotonic, so the normalised block's largest magnitude is
+// that maximum times the factor, rounded), the block exponent e is the
+// smallest with amax <= 448 * 2^e (read off the fp32 bits of amax), and each
+// normalised value is scaled by 2^-e (exact) and rounded to E4M3 by the
+// hardware's packed conversion.  Codes replace the bf16 row (8 bytes per
+// lane).  A head's D/32 scale bytes are gathered into its first lane (DPP
+// row shifts) and written with one 4-byte (D = 128) or 2-byte (D = 64)
+// store into the q, k or v scale tensor: single-byte stores from every
+// block cost the kernel about as much as all of its other stores together.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -86,13 +100,72 @@ __device__ __forceinline__ void load_state8(const T* state_in, int64_t s, int P,
     }
 }
 
-template <typename T, int D>
+typedef short short2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// E8M0 scale byte of a block whose largest magnitude is amax (>= 0): e + 127
+// with e the smallest integer such that amax <= 448 * 2^e = 1.75 * 2^(e+8),
+// clamped to [-127, 127].  For amax = (1 + m/2^23) 2^(E-127) that is
+// e = E - 135, plus one when the mantissa exceeds 0.75 (m > 0x600000).
+__device__ __forceinline__ int mx_scale_byte(uint32_t amax_bits) {
+    const int E = (int)(amax_bits >> 23);
+    const int e = E - 135 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return e < -127 ? 0 : e + 127;   // the largest E (254) gives e = 120
+}
+
+// Largest magnitude of the 8 values of a lane, and over the 4 lanes of its
+// 32-channel block (all 64 lanes must call it).
+__device__ __forceinline__ float block_amax(const float v[8]) {
+    float am = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(v[e]));
+    am = __builtin_fmaxf(am, __shfl_xor(am, 1, 64));
+    return __builtin_fmaxf(am, __shfl_xor(am, 2, 64));
+}
+
+// 8 normalised values of one lane as MXFP8 codes, with their block's
+// largest magnitude amax (see the header).  `scale` points at the head's
+// first scale byte of the token; lanes with `head_lane` (the head's first
+// lane) write the head's D/32 scale bytes.  All 64 lanes must call it.
+template <int D>
+__device__ __forceinline__ void store_mx8(uint8_t* codes, uint8_t* scale, bool active,
+                                          bool head_lane, const float v[8], float amax) {
+    static_assert(D == 64 || D == 128, "a head is 8 or 16 lanes");
+    const int sb = mx_scale_byte(__builtin_bit_cast(uint32_t, amax));
+    const float inv = __builtin_bit_cast(float, (uint32_t)(254 - sb) << 23);   // 2^-(sb-127)
+    short2_t lo = {0, 0}, hi = {0, 0};
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[0] * inv, v[1] * inv, 1.0f, false);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[2] * inv, v[3] * inv, 1.0f, true);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, v[4] * inv, v[5] * inv, 1.0f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(hi, v[6] * inv, v[7] * inv, 1.0f, true);
+    // the scale bytes of the blocks 4, 8, 12 lanes on, within the row of 16
+    const uint32_t b0 = (uint32_t)sb;
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b0, 0x104, 0xF, 0xF, false);
+    uint32_t word = b0 | (b1 << 8);
+    if constexpr (D == 128) {
+        const uint32_t b2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b0, 0x108, 0xF, 0xF, false);
+        const uint32_t b3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)b0, 0x10C, 0xF, 0xF, false);
+        word |= (b2 << 16) | (b3 << 24);
+    }
+    if (active) {
+        const u32x2_t w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(codes));
+        if (head_lane) {
+            if constexpr (D == 128) *reinterpret_cast<uint32_t*>(scale) = word;
+            else *reinterpret_cast<uint16_t*>(scale) = (uint16_t)word;
+        }
+    }
+}
+
+template <typename T, int D, bool MX = false>
 __global__ void __launch_bounds__(kConvThreads)
-conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict__ y,
+conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restrict__ yv,
             const T* __restrict__ state_in, const int32_t* __restrict__ cu, int num_seqs,
             int T_len, int64_t N, int P, int HD, float l2_eps, int tiles, int tiles_per_xcd,
-            int cblocks) {
+            int cblocks, uint8_t* __restrict__ sq, uint8_t* __restrict__ sk,
+            uint8_t* __restrict__ sv) {
     constexpr int TT = ConvTile<T>::TT;
+    static_assert(!MX || sizeof(T) == 2, "MXFP8 output from bf16 inputs");
     using Raw8 = typename RawVec<T, 8>::type;
     // Block -> (token tile, channel block).  Blocks go to the 8 XCDs round
     // robin, so XCD k gets the blocks k, k+8, ...: they are given a contiguous
@@ -108,6 +181,33 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
     const int64_t t0 = (int64_t)tile * TT;
     const int64_t t1 = t0 + TT < N ? t0 + TT : N;
     const bool is_qk = c0 < 2 * HD;   // uniform over the D/8 lanes of a head
+    // output of token t: the bf16 / fp32 row, or its MXFP8 codes and scales
+    uint8_t* scale_row = nullptr;
+    if constexpr (MX) {
+        const int part = c0 / HD;
+        scale_row = (part == 0 ? sq : (part == 1 ? sk : sv)) + (c0 - part * HD) / 32;
+    }
+    const bool head_lane = (threadIdx.x & (D / 8 - 1)) == 0;
+    // the L2 step and the store of token t: sum of squares over the head,
+    // then q and k scaled by 1/sqrt(ss + eps), then the bf16 / fp32 row or
+    // its MXFP8 codes and scales
+    auto finish = [&](int64_t t, float (&out)[8], float ss) {
+        float am = 0.f;
+        if constexpr (MX) am = block_amax(out);
+        ss = group_sum<D / 8>(ss);
+        if (is_qk) {
+            const float inv = rsqrt_nr(ss + l2_eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] *= inv;
+            am *= inv;
+        }
+        if constexpr (MX) {
+            store_mx8<D>(static_cast<uint8_t*>(yv) + t * P + c0, scale_row + t * (HD / 32),
+                         active, head_lane, out, am);
+        } else {
+            if (active) store8_nt(static_cast<T*>(yv) + t * P + c0, out);
+        }
+    };
 
     float wt[8][4];
 #pragma unroll
@@ -159,13 +259,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
                     win[e][1] = win[e][2];
                     win[e][2] = xv[e];
                 }
-                ss = group_sum<D / 8>(ss);
-                if (is_qk) {
-                    const float inv = rsqrt_nr(ss + l2_eps);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) out[e] *= inv;
-                }
-                if (active) store8_nt(y + (t0 + grp * G + j) * P + c0, out);
+                finish(t0 + grp * G + j, out, ss);
             }
         };
         Raw8 ra[G], rb[G];
@@ -235,13 +329,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, T* __restrict_
             win[e][1] = win[e][2];
             win[e][2] = xv[e];
         }
-        ss = group_sum<D / 8>(ss);
-        if (is_qk) {
-            const float inv = rsqrt_nr(ss + l2_eps);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] *= inv;
-        }
-        if (active) store8_nt(y + t * P + c0, out);
+        finish(t, out, ss);
     }
 }
 
@@ -279,10 +367,11 @@ conv_state_kernel(const T* __restrict__ x, const T* state_in, T* state_out,
     store8(p + 16, v + 16);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool MX = false>
 hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* state_in,
                          void* state_out, const int32_t* cu, int num_seqs, int T_len,
-                         int64_t N, int H, float l2_eps, hipStream_t s) {
+                         int64_t N, int H, float l2_eps, hipStream_t s, void* sq = nullptr,
+                         void* sk = nullptr, void* sv = nullptr) {
     const int P = 3 * H * D;
     const unsigned cblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
     if (N > 0) {
@@ -291,9 +380,10 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
         const int64_t per_xcd = (tiles + 7) / 8;
         const int64_t blocks = 8 * per_xcd * cblocks;
         if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((conv_kernel<T, D>), dim3((unsigned)blocks), dim3(kConvThreads), 0, s,
-                           (const T*)x, w, (T*)y, (const T*)state_in, cu, num_seqs, T_len, N, P,
-                           H * D, l2_eps, (int)tiles, (int)per_xcd, (int)cblocks);
+        hipLaunchKernelGGL((conv_kernel<T, D, MX>), dim3((unsigned)blocks), dim3(kConvThreads), 0,
+                           s, (const T*)x, w, y, (const T*)state_in, cu, num_seqs, T_len, N, P,
+                           H * D, l2_eps, (int)tiles, (int)per_xcd, (int)cblocks, (uint8_t*)sq,
+                           (uint8_t*)sk, (uint8_t*)sv);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -321,6 +411,18 @@ hipError_t launch_conv(const void* x, const float* w, void* y, const void* state
                                                H, l2_eps, s)
                    : launch_conv_t<__bf16, 128>(x, w, y, state_in, state_out, cu, num_seqs, T,
                                                 N, H, l2_eps, s);
+}
+
+hipError_t launch_conv_mxfp8(const void* x, const float* w, void* codes, void* q_scale,
+                             void* k_scale, void* v_scale, const void* state_in, void* state_out,
+                             const int32_t* cu, int num_seqs, int T, int64_t N, int H, int D,
+                             float l2_eps, hipStream_t s) {
+    return D == 64 ? launch_conv_t<__bf16, 64, true>(x, w, codes, state_in, state_out, cu,
+                                                     num_seqs, T, N, H, l2_eps, s, q_scale,
+                                                     k_scale, v_scale)
+                   : launch_conv_t<__bf16, 128, true>(x, w, codes, state_in, state_out, cu,
+                                                      num_seqs, T, N, H, l2_eps, s, q_scale,
+                                                      k_scale, v_scale);
 }
 
 }  // namespace kda

@@ -14,6 +14,12 @@ hipError_t launch_conv(const void* x, const float* w, void* y, const void* state
                        void* state_out, const int32_t* cu, int num_seqs, int T, int64_t N,
                        int H, int D, int dtype, float l2_eps, hipStream_t s);
 
+// kda_conv with MXFP8 output: codes [N, 3*H*D], scales [N, H, D/32] per part.
+hipError_t launch_conv_mxfp8(const void* x, const float* w, void* codes, void* q_scale,
+                             void* k_scale, void* v_scale, const void* state_in, void* state_out,
+                             const int32_t* cu, int num_seqs, int T, int64_t N, int H, int D,
+                             float l2_eps, hipStream_t s);
+
 hipError_t launch_decode(const void* x, const float* w, void* conv_state, const void* g,
                          const void* beta, float* state, void* o, int B, int H, int D,
                          int dtype, float l2_eps, hipStream_t s);

@@ -185,8 +185,10 @@ def main():
     # every kernel of the counter run against its algorithmic bytes
     pb = bench.prefill_bytes(65536, 96, 128, 1)
     kinds = [
-        ("conv (kda_conv, T=65536)", "conv_kernel", pb["conv"]),
+        ("conv (kda_conv, T=65536)", "conv_kernelIDF16bLi128ELb0E", pb["conv"]),
         ("chunk (kda_chunk_prefill, chunk 16, T=65536)", CHUNK_TAG, pb["chunk"]),
+        ("conv MXFP8 out (kda_conv_mxfp8, T=65536)", "conv_kernelIDF16bLi128ELb1E",
+         bench.mxfp8_conv_bytes(65536, 96, 128)),
         ("chunk MXFP8 (kda_chunk_prefill_mxfp8, T=65536)", MX_TAG,
          bench.mxfp8_chunk_bytes(65536, 96, 128, 1)),
         ("gated norm (kda_gated_norm, T=65536)", "gated_norm_kernel", pb["norm"]),

@@ -30,7 +30,8 @@ def L():
 
 
 def test_header_declares_the_calls():
-    assert declared() == ["kda_chunk_prefill", "kda_chunk_prefill_mxfp8", "kda_conv", "kda_decode_multi", "kda_decode_step",
+    assert declared() == ["kda_chunk_prefill", "kda_chunk_prefill_mxfp8", "kda_conv",
+                          "kda_conv_mxfp8", "kda_decode_multi", "kda_decode_step",
                           "kda_gated_norm", "kda_last_error", "kda_mla_decode",
                           "kda_mla_decode_workspace_bytes", "kda_version"]
 
@@ -65,6 +66,30 @@ def test_conv_argument_checks(L):
     assert conv(L, si=A + 256 * MB, so=A + 256 * MB + 16, B=1) == INVALID  # partial alias
     assert "kda_conv" in kda.kda_last_error()
     assert conv(L, B=0) == OK                                # nothing to do, nothing launched
+
+
+def conv_mx(L, x=A, w=A + 8 * MB, y=A + 64 * MB, qs=A + 80 * MB, ks=A + 81 * MB, vs=A + 82 * MB,
+            si=None, so=None, cu=None, ns=0, B=1, T=8, H=2, D=128, eps=1e-6):
+    return L.kda_conv_mxfp8(x, w, y, qs, ks, vs, si, so, cu, ns, B, T, H, D, eps, None)
+
+
+def test_conv_mxfp8_argument_checks(L):
+    assert conv_mx(L, x=None) == INVALID
+    assert conv_mx(L, ks=None) == INVALID
+    assert conv_mx(L, D=96) == UNSUPPORTED
+    assert conv_mx(L, H=0) == INVALID
+    assert conv_mx(L, eps=0.0) == INVALID
+    assert conv_mx(L, y=A + 8) == INVALID                    # misaligned codes
+    assert conv_mx(L, ks=A + 81 * MB + 2) == INVALID         # a head's 4 scale bytes: 4-aligned
+    assert conv_mx(L, ks=A + 81 * MB + 2, D=64) not in (INVALID, UNSUPPORTED)  # 2-aligned
+    assert conv_mx(L, y=A + 1024) == INVALID                 # codes overlap x
+    assert conv_mx(L, qs=A + 64 * MB + 100) == INVALID       # a scale tensor inside the codes
+    assert conv_mx(L, vs=A + 81 * MB + 8) == INVALID         # two scale tensors overlap
+    assert conv_mx(L, cu=A + 128 * MB, B=2) == INVALID       # varlen needs B == 1
+    assert conv_mx(L, si=A + 256 * MB, so=A + 256 * MB + 16, B=1) == INVALID
+    assert conv_mx(L, so=A + 80 * MB) == INVALID             # state over the q scales
+    assert conv_mx(L, B=0) == OK
+    assert "kda_conv_mxfp8" in kda.kda_last_error()
 
 
 def chunk(L, q=A, k=A + 256, v=A + 512, stride=3 * 2 * 128, g=A + 64 * MB, b=A + 96 * MB,

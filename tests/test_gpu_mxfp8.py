@@ -176,3 +176,136 @@ def test_chunk_prefill_mxfp8_full_size_sampled_heads():
                            list(range(len(heads))))
     assert report("o", f64(o[:, idx]), o_ref, TOL["bf16"]) <= TOL["bf16"]
     assert report("S_T", f64(sT[:, idx]), S_ref, TOL["bf16"]) <= TOL["bf16"]
+
+
+# --------------------------------------------------------- conv with MXFP8 output
+def _check_codes(gpu_codes, gpu_scales, ref32, tag):
+    """GPU MXFP8 encoding of a row set against the oracle's encoding of the
+    oracle's values rounded to fp32 (the kernel's precision).  The two agree
+    except where a value sits close to a decision: the block's largest
+    magnitude within 1e-5 (relative) of a scale boundary 448 * 2^k, or an
+    element within 1e-6 of the block's range (448 in scaled units) of a
+    midpoint between neighbouring E4M3 values; there the GPU may take either
+    side.  The element window is absolute because the kernel's fp32 conv sum
+    carries rounding error of the order of 2^-24 times its tap magnitudes, so
+    a small output (a sum that cancels) can be off by far more than its own
+    relative precision."""
+    rc, rs = kda_ref.mxfp8_encode(ref32)
+    gs = gpu_scales.astype(np.int64)
+    amax = np.abs(ref32).reshape(*ref32.shape[:-1], -1, 32).max(-1)
+    near_edge = (kda_ref.e8m0_exponent_for(amax * (1 - 1e-5))
+                 != kda_ref.e8m0_exponent_for(amax * (1 + 1e-5)))
+    bad_scale = (gs != rs) & ~near_edge
+    assert not bad_scale.any(), f"{tag}: {bad_scale.sum()} scale bytes differ away from a boundary"
+    same_scale = np.repeat(gs == rs, 32, axis=-1)
+    gv, rv = kda_ref.e4m3_value(gpu_codes), kda_ref.e4m3_value(rc)
+    diff = (gv != rv) & same_scale
+    y = np.ldexp(ref32, -(np.repeat(rs.astype(np.int64), 32, axis=-1) - 127))
+    dy = 1e-6 * 448.0
+    lo = kda_ref.e4m3_round(np.clip(y - dy, -448, 448))
+    hi = kda_ref.e4m3_round(np.clip(y + dy, -448, 448))
+    near_tie = kda_ref.e4m3_value(lo) != kda_ref.e4m3_value(hi)
+    either = (gv == kda_ref.e4m3_value(lo)) | (gv == kda_ref.e4m3_value(hi))
+    bad = diff & ~(near_tie & either)
+    if bad.any():
+        idx = np.argwhere(bad)
+        toks = np.unique(idx[:, 0])
+        print(f"  {tag}: {bad.sum()} codes differ away from a tie, tokens {toks[:20]} .. "
+              f"({len(toks)} tokens), channels {np.unique(idx[:, -1])[:16]}", flush=True)
+        for i in idx[:6]:
+            i = tuple(i)
+            print(f"    at {i}: gpu {gv[i]!r} ref {rv[i]!r} scaled {y[i]!r} "
+                  f"code {int(gpu_codes[i]):#04x}/{int(rc[i]):#04x}", flush=True)
+    assert not bad.any(), f"{tag}: codes differ away from a tie"
+    n = diff.sum()
+    print(f"  {tag}: {n} of {diff.size} codes at a near-tie took the other side; "
+          f"{(gs != rs).sum()} scale bytes at a boundary", flush=True)
+    assert n <= max(4, 1e-4 * diff.size)
+
+
+CONV_CASES = [
+    # (D, H, lengths, varlen, with state_in)
+    (128, 3, [50, 50], False, True),
+    (128, 2, [0, 1, 2, 3, 5, 40, 300, 0, 33], True, True),
+    (64, 5, [129, 31], True, True),
+    (128, 4, [1000], False, False),
+]
+
+
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: f"D{c[0]}-H{c[1]}-{len(c[2])}seq")
+def test_conv_mxfp8(case):
+    D_, H, lengths, varlen, with_state = case
+    print(f"mxfp8 conv case={case}", flush=True)
+    P = 3 * H * D_
+    N, S = sum(lengths), len(lengths)
+    x = (torch.randn((max(N, 1), P), generator=_gen(40), device="cuda")).to(torch.bfloat16)
+    x = x[:N].contiguous()
+    w = torch.randn((P, 4), generator=_gen(41), device="cuda") * 0.25
+    si = (torch.randn((S, P, 3), generator=_gen(42), device="cuda").to(torch.bfloat16)
+          if with_state else None)
+    so = torch.empty((S, P, 3), dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty((N, P), dtype=torch.uint8, device="cuda")
+    sc = [torch.empty((N, H, D_ // 32), dtype=torch.uint8, device="cuda") for _ in range(3)]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    kw = dict(conv_state_in=si, conv_state_out=so)
+    if varlen:
+        kw.update(cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"), num_seqs=S)
+        B, T = 1, N
+    else:
+        B, T = S, N // S
+    kda.kda_conv_mxfp8(x, w, codes, *sc, B, T, H, D_, **kw)
+    torch.cuda.synchronize()
+    xs, ws = f64(x), f64(w)
+    ref_y = np.zeros((N, 3, H, D_))
+    ref_s = np.zeros((S, P, 3))
+    for s in range(S):
+        t0, t1 = cu[s], cu[s + 1]
+        ys, ref_s[s] = c_oracle.short_conv_silu(xs[t0:t1], ws, None if si is None else f64(si)[s])
+        ys = ys.reshape(t1 - t0, 3, H, D_)
+        ys[:, :2] = kda_ref.l2norm(ys[:, :2])
+        ref_y[t0:t1] = ys
+    ref32 = ref_y.astype(np.float32).astype(np.float64)
+    gc = codes.cpu().numpy().reshape(N, 3, H, D_)
+    for part, name in enumerate("qkv"):
+        _check_codes(gc[:, part], sc[part].cpu().numpy(), ref32[:, part], name)
+    assert np.array_equal(f64(so), ref_s)                 # rolling state: copies of inputs
+    # decoded values against the fp64 oracle: within half an E4M3 step
+    dec = np.stack([kda_ref.mxfp8_decode(gc[:, p], sc[p].cpu().numpy()) for p in range(3)], 1)
+    assert report("y (decoded)", dec, ref_y, 0.05) <= 0.05
+
+
+def test_mxfp8_conv_then_chunk_matches_oracle_chain():
+    """kda_conv_mxfp8 -> kda_chunk_prefill_mxfp8 against the oracle's chain:
+    conv + L2 in fp64, the oracle's MXFP8 encoding of it (in fp32), decode,
+    then the fp64 recurrence."""
+    H, T = 4, 777
+    P, HD = 3 * H * D, H * D
+    x = torch.randn((T, P), generator=_gen(50), device="cuda").to(torch.bfloat16)
+    w = torch.randn((P, 4), generator=_gen(51), device="cuda") * 0.25
+    g = -5.0 * torch.rand((T, H, D), generator=_gen(52), device="cuda")
+    gc, gsc = synth.mxfp8_encode(g)
+    gc, gsc = gc.contiguous(), gsc.contiguous()
+    beta = torch.sigmoid(torch.randn((T, H), generator=_gen(53), device="cuda")).to(torch.bfloat16)
+    codes = torch.empty((T, P), dtype=torch.uint8, device="cuda")
+    sc = [torch.empty((T, H, 4), dtype=torch.uint8, device="cuda") for _ in range(3)]
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    kda.kda_conv_mxfp8(x, w, codes, *sc, 1, T, H, D)
+    kda.kda_chunk_prefill_mxfp8(codes[:, :HD], sc[0], codes[:, HD:2 * HD], sc[1],
+                                codes[:, 2 * HD:], sc[2], P, gc, gsc, beta, o, 1, T, H,
+                                final_state=sT)
+    torch.cuda.synchronize()
+    ys, _ = c_oracle.short_conv_silu(f64(x), f64(w), None)
+    ys = ys.reshape(T, 3, H, D)
+    ys[:, :2] = kda_ref.l2norm(ys[:, :2])
+    ref32 = ys.astype(np.float32).astype(np.float64)
+    q64, k64, v64 = (kda_ref.mxfp8_decode(*kda_ref.mxfp8_encode(ref32[:, p])) for p in range(3))
+    g64 = kda_ref.mxfp8_decode(gc.cpu().numpy(), gsc.cpu().numpy())
+    b64 = f64(beta)
+    o_ref = np.zeros((T, H, D))
+    S_ref = np.zeros((1, H, D, D))
+    for h in range(H):
+        o_ref[:, h], S_ref[0, h] = c_oracle.gated_delta_rule(q64[:, h], k64[:, h], v64[:, h],
+                                                             g64[:, h], b64[:, h], None)
+    assert report("o", f64(o), o_ref, TOL["bf16"]) <= TOL["bf16"]
+    assert report("S_T", f64(sT), S_ref, TOL["bf16"]) <= TOL["bf16"]
