@@ -300,8 +300,15 @@ def cpu_baseline(inp, spec, T_s, H_s):
     c_oracle.kda_prefill(xs, ws, gs, bs, zs, nw, [0, T_s], H_s, D)
     dt = time.perf_counter() - t0
     del np
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                       cpu)
+    except OSError:
+        pass
     return {"value": T_s * H_s / H / dt, "unit": "tokens/s", "cores": min(nthr, H_s),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu,
             "sample": (f"C fp64 oracle, whole prefill path (conv, L2, recurrence, gated norm) on "
                        f"the first {T_s} tokens of {H_s} of the {H} heads, {dt:.1f} s; "
                        f"scaled to tokens/s of the {H}-head layer")}
@@ -422,6 +429,7 @@ def main():
         k_ms["conv"] += e[0].elapsed_time(e[1]) / args.steps
         k_ms["chunk"] += e[1].elapsed_time(e[2]) / args.steps
         k_ms["norm"] += e[2].elapsed_time(e[3]) / args.steps
+    chunk_each = sorted(e[1].elapsed_time(e[2]) for e in ev)
     log(f"timed prefill: {ms_step:.3f} ms/step; kernels {k_ms}")
 
     nbytes = prefill_bytes(N, H, D, 1)
@@ -450,6 +458,8 @@ def main():
                      "kernel": CHUNK_KERNEL,
                      "algorithmic_bytes_per_launch": nbytes["chunk"],
                      "avg_launch_ms": k_ms["chunk"],
+                     "launch_ms_median_min_max": [chunk_each[len(chunk_each) // 2],
+                                                  chunk_each[0], chunk_each[-1]],
                      "mfma_tflops_algorithmic": flops / (k_ms["chunk"] * 1e-3) / 1e12,
                      "mfma_frac": flops / (k_ms["chunk"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "kernels_ms": k_ms,

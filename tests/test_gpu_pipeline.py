@@ -73,6 +73,52 @@ def test_stress_long_carry_1M_tokens():
     _run_config(synth.STRESS["long_carry_1M"], heads=[0, 1])
 
 
+def test_chunk_1M_tokens_96_heads_sampled():
+    """The chunk kernel in the launch the 1M-token throughput figure is taken
+    in: one sequence of 1,048,576 tokens with all 96 heads (token offsets up
+    to about 77 GB into the q|k|v buffer), inputs filled on the device with
+    the workloads' value ranges (q, k with unit norm on average, v in [-1, 1],
+    log-decay in [-5, 0], beta in (0.1, 0.9)); three heads, the first, a
+    middle and the last, against the oracle, one host thread per head."""
+    from concurrent.futures import ThreadPoolExecutor
+    N, H, D = 1 << 20, 96, 128
+    HD = H * D
+    heads = [0, 50, 95]
+    torch.cuda.empty_cache()
+    print(f"chunk T={N} H={H}: filling inputs on the device", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2024)
+    y_qkv = torch.empty((N, 3 * HD), dtype=torch.bfloat16, device="cuda")
+    y_qkv[:, :2 * HD].uniform_(-0.15, 0.15, generator=gen)
+    y_qkv[:, 2 * HD:].uniform_(-1.0, 1.0, generator=gen)
+    g = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda").uniform_(-5.0, 0.0,
+                                                                               generator=gen)
+    beta = torch.empty((N, H), dtype=torch.bfloat16, device="cuda").uniform_(0.1, 0.9,
+                                                                             generator=gen)
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    kda.kda_chunk_prefill(y_qkv[:, :HD], y_qkv[:, HD:2 * HD], y_qkv[:, 2 * HD:], 3 * HD, g, beta,
+                          o, 1, N, H, D, D, chunk=16, final_state=sT)
+    torch.cuda.synchronize()
+    print("  GPU done; copying the sampled heads", flush=True)
+    cols = lambda part, h: slice(part * HD + h * D, part * HD + (h + 1) * D)
+    ins = {h: (f64(y_qkv[:, cols(0, h)]), f64(y_qkv[:, cols(1, h)]), f64(y_qkv[:, cols(2, h)]),
+               f64(g[:, h]), f64(beta[:, h])) for h in heads}
+    o_gpu = {h: f64(o[:, h]) for h in heads}
+    s_gpu = {h: f64(sT[0, h]) for h in heads}
+    del y_qkv, g, beta, o, sT
+    torch.cuda.empty_cache()
+
+    def one(h):
+        return h, c_oracle.gated_delta_rule(*ins[h], None)
+
+    with ThreadPoolExecutor(len(heads)) as ex:
+        for h, (o_ref, s_ref) in ex.map(one, heads):
+            print(f"  head {h}:", flush=True)
+            assert report("o", o_gpu[h], o_ref, TOL["bf16"]) <= TOL["bf16"]
+            assert report("S_T", s_gpu[h], s_ref, TOL["bf16"]) <= TOL["bf16"]
+
+
 def test_config4_decode_64_steps_sampled_pairs():
     spec = synth.CONFIGS[4]
     B, H, D, steps = spec.B, spec.H, spec.D, spec.steps
