@@ -26,8 +26,10 @@
 // hardware's packed conversion.  Codes replace the bf16 row (8 bytes per
 // lane).  A head's D/32 scale bytes are gathered into its first lane (DPP
 // row shifts) and written with one 4-byte (D = 128) or 2-byte (D = 64)
-// store into the q, k or v scale tensor: single-byte stores from every
-// block cost the kernel about as much as all of its other stores together.
+// store into the q, k or v scale tensor.  With MXFP8 output a block covers
+// 4096 channels (512 threads), so that its scale bytes of a token are whole
+// 128-byte lines: lines shared between blocks (2048 channels write 64
+// bytes of a 384-byte row) made the kernel about 60 % slower.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -157,8 +159,11 @@ __device__ __forceinline__ void store_mx8(uint8_t* codes, uint8_t* scale, bool a
     }
 }
 
+template <bool MX>
+constexpr int conv_threads() { return MX ? 2 * kConvThreads : kConvThreads; }
+
 template <typename T, int D, bool MX = false>
-__global__ void __launch_bounds__(kConvThreads)
+__global__ void __launch_bounds__(conv_threads<MX>())
 conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restrict__ yv,
             const T* __restrict__ state_in, const int32_t* __restrict__ cu, int num_seqs,
             int T_len, int64_t N, int P, int HD, float l2_eps, int tiles, int tiles_per_xcd,
@@ -175,7 +180,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
     const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
     const int tile = xcd * tiles_per_xcd + li / cblocks;
     if (tile >= tiles) return;
-    const int cbase = (li % cblocks) * kConvChannels;   // the block's first channel
+    const int cbase = (li % cblocks) * (conv_threads<MX>() * 8);   // the block's first channel
     const int c0 = cbase + threadIdx.x * 8;
     const bool active = c0 < P;
     const int64_t t0 = (int64_t)tile * TT;
@@ -220,7 +225,8 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
     // Fast path (uniform over the block): the strip and its halo lie inside one
     // sequence, so every window reads plain inputs.
     if (sr.start <= t0 - 3 && sr.end >= t0 + TT) {
-        constexpr int G = ConvTile<T>::G, NG = TT / G;
+        // MXFP8 output: half-size groups keep 512 threads within 256 VGPRs
+        constexpr int G = MX ? ConvTile<T>::G / 2 : ConvTile<T>::G, NG = TT / G;
         static_assert(TT % G == 0, "whole groups per strip");
         // rows t0-3 .. of this strip from the block's first channel (a
         // wave-uniform resource; the lane's channels go in the offset).  The
@@ -373,14 +379,15 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
                          int64_t N, int H, float l2_eps, hipStream_t s, void* sq = nullptr,
                          void* sk = nullptr, void* sv = nullptr) {
     const int P = 3 * H * D;
-    const unsigned cblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
+    constexpr int threads = conv_threads<MX>();
+    const unsigned cblocks = (unsigned)((P + threads * 8 - 1) / (threads * 8));
     if (N > 0) {
         constexpr int TT = ConvTile<T>::TT;
         const int64_t tiles = (N + TT - 1) / TT;
         const int64_t per_xcd = (tiles + 7) / 8;
         const int64_t blocks = 8 * per_xcd * cblocks;
         if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((conv_kernel<T, D, MX>), dim3((unsigned)blocks), dim3(kConvThreads), 0,
+        hipLaunchKernelGGL((conv_kernel<T, D, MX>), dim3((unsigned)blocks), dim3(threads), 0,
                            s, (const T*)x, w, y, (const T*)state_in, cu, num_seqs, T_len, N, P,
                            H * D, l2_eps, (int)tiles, (int)per_xcd, (int)cblocks, (uint8_t*)sq,
                            (uint8_t*)sk, (uint8_t*)sv);
@@ -388,7 +395,8 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
         if (e != hipSuccess) return e;
     }
     if (state_out != nullptr && num_seqs > 0) {
-        hipLaunchKernelGGL((conv_state_kernel<T>), dim3((unsigned)num_seqs, cblocks),
+        const unsigned sblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
+        hipLaunchKernelGGL((conv_state_kernel<T>), dim3((unsigned)num_seqs, sblocks),
                            dim3(kConvThreads), 0, s, (const T*)x, (const T*)state_in,
                            (T*)state_out, cu, T_len, P);
         return hipGetLastError();
