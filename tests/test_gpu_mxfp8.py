@@ -309,3 +309,32 @@ def test_mxfp8_conv_then_chunk_matches_oracle_chain():
                                                              g64[:, h], b64[:, h], None)
     assert report("o", f64(o), o_ref, TOL["bf16"]) <= TOL["bf16"]
     assert report("S_T", f64(sT), S_ref, TOL["bf16"]) <= TOL["bf16"]
+
+
+def test_conv_mxfp8_full_size_sampled_heads():
+    """kda_conv_mxfp8 on the 65,536-token, 96-head prefill workload (the launch
+    the MXFP8 step is timed in: nine 4,096-channel blocks, all lanes active),
+    three heads (q, k and v channels) against the oracle's encoding."""
+    from tests.kda_testlib import head_channels
+    spec = synth.CONFIGS[2]
+    H, D_ = spec.H, spec.D
+    heads = [0, 47, 95]
+    print(f"mxfp8 conv full size {spec.name} heads={heads}", flush=True)
+    inp = synth.prefill_inputs(spec, device="cuda")
+    x, w = inp["x"], inp["conv_w"]
+    N, P = x.shape
+    codes = torch.empty((N, P), dtype=torch.uint8, device="cuda")
+    sc = [torch.empty((N, H, D_ // 32), dtype=torch.uint8, device="cuda") for _ in range(3)]
+    kda.kda_conv_mxfp8(x, w, codes, *sc, 1, N, H, D_)
+    torch.cuda.synchronize()
+    cols = torch.as_tensor(head_channels(H, D_, heads), device="cuda")
+    ys, _ = c_oracle.short_conv_silu(f64(x.index_select(1, cols)), f64(w.index_select(0, cols)),
+                                     None)
+    ys = ys.reshape(N, 3, len(heads), D_)
+    ys[:, :2] = kda_ref.l2norm(ys[:, :2])
+    ref32 = ys.astype(np.float32).astype(np.float64)
+    gc = codes.index_select(1, cols).cpu().numpy().reshape(N, 3, len(heads), D_)
+    hidx = torch.tensor(heads, device="cuda")
+    for part, name in enumerate("qkv"):
+        _check_codes(gc[:, part], sc[part].index_select(1, hidx).cpu().numpy(), ref32[:, part],
+                     name)
