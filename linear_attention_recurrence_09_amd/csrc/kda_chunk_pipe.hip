@@ -42,6 +42,17 @@
 //    each consumer: "slot released"), so producers run ahead of the consumers
 //    by up to the ring depth.  Every wait is bounded; a wait that runs out
 //    stops the workgroup and its final state is written as NaN.
+//
+// MXFP8 inputs ("Inside Kimi K3", model at a glance: MXFP8 activations, read
+// as OCP microscaling).  A second instantiation takes q, k, v and g as E4M3
+// code bytes with one E8M0 scale byte per 32 channels.  Only the producers'
+// loads and unpacking differ: a lane loads one 16-bit code word per token and
+// tensor, and one scale byte per tensor and chunk (lane (block b, token t) of
+// row b); token t's scale is broadcast across the row by DPP and is the scale
+// operand of the scaled fp8 -> fp32 conversion, which yields the exact
+// values; V codes are decoded the same way and stored to the slot as bf16
+// (exact).  Everything after that is the bf16 kernel's code, so on the
+// decoded values both give bitwise equal results.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 

@@ -29,7 +29,8 @@
 // store into the q, k or v scale tensor.  With MXFP8 output a block covers
 // 4096 channels (512 threads), so that its scale bytes of a token are whole
 // 128-byte lines: lines shared between blocks (2048 channels write 64
-// bytes of a 384-byte row) made the kernel about 60 % slower.
+// bytes of a 384-byte row) made the kernel about 50 % slower.  It streams
+// 8-row groups instead of 16, which keeps 512 threads within 256 VGPRs.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
