@@ -231,6 +231,31 @@ __device__ __forceinline__ void back_subst(float (&y)[16], const float (&np)[16]
     back_subst_steps<15>(y, np);
 }
 
+// The same solve split over the four 16-lane rows (one chunk per wave): lane
+// c of row q holds rows r = q + 4k (k = 0..3) of column c, of -N in np[k] and
+// of Y in y[k] (started at column c of I, so Y comes out with its diagonal).
+// Step M fetches the finished entry Y[M][c] from its owner row (M % 4, slot
+// M / 4; one ds_bpermute) and updates the slots k < ceil(M / 4) of every row:
+// the rows r >= M among them add -N[r][M] = 0 (the masked entries are stored
+// as zeros).  36 broadcast multiply-adds instead of 120.
+template <int M>
+__device__ __forceinline__ void back_subst_split_steps(float (&y)[4], const float (&np)[4],
+                                                       int lr) {
+    if constexpr (M >= 1) {
+        const float piv = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(((M & 3) * 16 + lr) * 4,
+                                                __builtin_bit_cast(int, y[M / 4])));
+#pragma unroll
+        for (int k = 0; k < (M + 3) / 4; ++k) fmac_bcast<M>(y[k], np[k], piv);
+        back_subst_split_steps<M - 1>(y, np, lr);
+    }
+}
+
+__device__ __forceinline__ void back_subst_split(float (&y)[4], const float (&np)[4], int lr) {
+    asm volatile("s_nop 1" ::"v"(np[0]), "v"(np[1]), "v"(np[2]), "v"(np[3]));
+    back_subst_split_steps<15>(y, np, lr);
+}
+
 // Rows of the state tiles KT .. NKT-1 times their decay e^{G_15}: row i of
 // tile KT is channel 16 KT + 4q + i; its decay sits in lane 2 KT + i/2 of the
 // lane's own 16-lane row, component i % 2.
@@ -653,7 +678,33 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             // batches (all full: only the last batch can be short)
             const int n_in = nch - kBatch * bt < kBatch ? nch - kBatch * bt : kBatch;
             const int counted = go ? batch_count(&batch[bslot], lane) : -1;
-            if (counted == kBatch * (bt / kNBatch) + n_in - 1) {
+            if constexpr (kBatch == 1) {
+                // one chunk: the four lane rows share its solve (see
+                // back_subst_split) and each writes its rows of M'
+                if (counted == bt / kNBatch) {
+                    const float* col = nbp + (mine * 16 + lr) * 16;
+                    const float* bet = btp + mine * 16;
+                    float np[4], y[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        np[k] = col[lq + 4 * k];
+                        y[k] = lq + 4 * k == lr ? 1.f : 0.f;
+                    }
+                    back_subst_split(y, np, lr);
+                    // M'[lr][4k+q] = Y[4k+q][lr] beta_{4k+q}: entry q of the
+                    // 4-entry group k of lane (k, lr) of the 16x16x16 A operand
+                    char* slot_g = smem + (cix % kRing) * SLOT;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        *reinterpret_cast<__bf16*>(slot_g + Cfg::O_MP + (16 * k + lr) * 8 + lq * 2) =
+                            (__bf16)(y[k] * bet[4 * k + lq]);
+                    // publish the chunk after every lane's M' writes (the
+                    // release waits for them)
+                    if (lq == 0 && lr == 0)
+                        __hip_atomic_store(&ready[cix % kRing], cix / kRing + 1, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+            } else if (counted == kBatch * (bt / kNBatch) + n_in - 1) {
                 // lane (row, c): chunk kBatch bt + row / RPC, column c of -N,
                 // then of Y - I
                 const int gi = lq / RPC;
