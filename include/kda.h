@@ -37,7 +37,14 @@
  *   1 and T must equal cu_seqlens[num_seqs]; sequence i occupies tokens
  *   [cu_seqlens[i], cu_seqlens[i+1]).  When it is null, there are B sequences
  *   of T tokens each (num_seqs is ignored and taken as B).  The offsets live
- *   in device memory and are not read on the host.
+ *   in device memory and are not read on the host.  The kernels clamp each
+ *   sequence's range to [0, T] (start first, then end to [start, T]), so
+ *   offsets that break the rules give wrong results but never an access out
+ *   of bounds.  Debug check: with the environment variable
+ *   KDA_CHECK_CU_SEQLENS set to a value other than 0, the calls that take
+ *   cu_seqlens copy it to the host (waiting for the stream) and return
+ *   KDA_ERR_INVALID_ARG, launching nothing, unless it starts at 0, never
+ *   decreases and ends at T.
  * - Shapes: H >= 1 heads; head sizes D, DK, DV in {64, 128}.
  */
 #ifndef KDA_H_

@@ -101,6 +101,31 @@ def _check(fn, rc):
         raise KdaError(fn, rc, kda_last_error())
 
 
+def _extent(t):
+    """Elements reachable from t's data pointer to the end of its storage."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _need(fn, **sizes):
+    """Raise unless each named tensor (name=(tensor, elements)) reaches at
+    least the given number of elements from its data pointer, so a shape
+    that disagrees with the sizes passed to the C ABI never reaches a kernel."""
+    for name, (t, n) in sizes.items():
+        if t is not None and n > 0 and _extent(t) < n:
+            raise ValueError(f"{fn}: {name} holds {_extent(t)} elements from its data "
+                             f"pointer, {n} needed")
+
+
+def _tokens(B, T, cu_seqlens, num_seqs):
+    """(sequences, tokens) of a dense (B, T) or packed (cu_seqlens) batch."""
+    if cu_seqlens is not None:
+        if cu_seqlens.numel() < num_seqs + 1:
+            raise ValueError(f"cu_seqlens holds {cu_seqlens.numel()} offsets, "
+                             f"{num_seqs + 1} needed")
+        return num_seqs, T
+    return B, B * T
+
+
 def _same_dtype(ref, *ts):
     for t in ts:
         if t is not None and t.dtype != ref.dtype:
@@ -120,6 +145,10 @@ def kda_conv(x, w, y, B, T, H, D, conv_state_in=None, conv_state_out=None, cu_se
     _f32(w)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    ns, N = _tokens(B, T, cu_seqlens, num_seqs)
+    P = 3 * H * D
+    _need("kda_conv", x=(x, N * P), y=(y, N * P), w=(w, P * 4),
+          conv_state_in=(conv_state_in, ns * P * 3), conv_state_out=(conv_state_out, ns * P * 3))
     _check("kda_conv", lib().kda_conv(_ptr(x), _ptr(w), _ptr(y), _ptr(conv_state_in),
                                       _ptr(conv_state_out), _ptr(cu_seqlens), num_seqs, B, T, H,
                                       D, _dtype(x), l2_eps, _stream(stream)))
@@ -140,6 +169,12 @@ def kda_chunk_prefill(q, k, v, qkv_token_stride, g, beta, o, B, T, H, DK, DV, ch
             raise TypeError("q, k, v must be GPU tensors of the per-token dtype")
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    ns, N = _tokens(B, T, cu_seqlens, num_seqs)
+    rows = (N - 1) * qkv_token_stride if N > 0 else 0
+    _need("kda_chunk_prefill", q=(q, rows + H * DK if N else 0), k=(k, rows + H * DK if N else 0),
+          v=(v, rows + H * DV if N else 0), g=(g, N * H * DK), beta=(beta, N * H),
+          o=(o, N * H * DV), initial_state=(initial_state, ns * H * DK * DV),
+          final_state=(final_state, ns * H * DK * DV))
     _check("kda_chunk_prefill",
            lib().kda_chunk_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), qkv_token_stride,
                                    _ptr(g), _ptr(beta), _ptr(o), _ptr(initial_state),
@@ -160,6 +195,12 @@ def kda_conv_mxfp8(x, w, y_codes, q_scale, k_scale, v_scale, B, T, H, D, conv_st
             raise TypeError("codes and scales must be uint8")
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    ns, N = _tokens(B, T, cu_seqlens, num_seqs)
+    P = 3 * H * D
+    _need("kda_conv_mxfp8", x=(x, N * P), w=(w, P * 4), y_codes=(y_codes, N * P),
+          q_scale=(q_scale, N * H * D // 32), k_scale=(k_scale, N * H * D // 32),
+          v_scale=(v_scale, N * H * D // 32), conv_state_in=(conv_state_in, ns * P * 3),
+          conv_state_out=(conv_state_out, ns * P * 3))
     _check("kda_conv_mxfp8",
            lib().kda_conv_mxfp8(_ptr(x), _ptr(w), _ptr(y_codes), _ptr(q_scale), _ptr(k_scale),
                                 _ptr(v_scale), _ptr(conv_state_in), _ptr(conv_state_out),
@@ -186,6 +227,13 @@ def kda_chunk_prefill_mxfp8(q, q_scale, k, k_scale, v, v_scale, qkv_token_stride
     _f32(initial_state, final_state)
     if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
+    ns, N = _tokens(B, T, cu_seqlens, num_seqs)
+    rows = (N - 1) * qkv_token_stride + H * 128 if N > 0 else 0
+    _need("kda_chunk_prefill_mxfp8", q=(q, rows), k=(k, rows), v=(v, rows),
+          q_scale=(q_scale, N * H * 4), k_scale=(k_scale, N * H * 4),
+          v_scale=(v_scale, N * H * 4), g=(g, N * H * 128), g_scale=(g_scale, N * H * 4),
+          beta=(beta, N * H), o=(o, N * H * 128), initial_state=(initial_state, ns * H * 128 * 128),
+          final_state=(final_state, ns * H * 128 * 128))
     _check("kda_chunk_prefill_mxfp8",
            lib().kda_chunk_prefill_mxfp8(q.data_ptr(), _ptr(q_scale), k.data_ptr(),
                                          _ptr(k_scale), v.data_ptr(), _ptr(v_scale),
@@ -199,6 +247,9 @@ def kda_decode_step(x, w, conv_state, g, beta, state, o, B, H, D, l2_eps=1e-6, s
     """One decode step; conv_state and state are updated in place."""
     _same_dtype(x, conv_state, g, beta, o)
     _f32(w, state)
+    P = 3 * H * D
+    _need("kda_decode_step", x=(x, B * P), w=(w, P * 4), conv_state=(conv_state, B * P * 3),
+          g=(g, B * H * D), beta=(beta, B * H), state=(state, B * H * D * D), o=(o, B * H * D))
     _check("kda_decode_step",
            lib().kda_decode_step(_ptr(x), _ptr(w), _ptr(conv_state), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(o), B, H, D, _dtype(x), l2_eps,
@@ -215,6 +266,11 @@ def kda_decode_multi(x, w, conv_state_in, g, beta, state_in, B, K, H, D, o=None,
     _f32(w, state_in, *(t for t in (state_out,) if t is not None))
     if n_tokens is not None and n_tokens.dtype != torch.int32:
         raise TypeError("n_tokens must be int32")
+    P = 3 * H * D
+    _need("kda_decode_multi", x=(x, B * K * P), w=(w, P * 4), conv_state_in=(conv_state_in, B * P * 3),
+          conv_state_out=(conv_state_out, B * P * 3), g=(g, B * K * H * D), beta=(beta, B * K * H),
+          state_in=(state_in, B * H * D * D), state_out=(state_out, B * H * D * D),
+          o=(o, B * K * H * D), n_tokens=(n_tokens, B))
     _check("kda_decode_multi",
            lib().kda_decode_multi(_ptr(x), _ptr(w), _ptr(conv_state_in), _ptr(conv_state_out),
                                   _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out), _ptr(o),
@@ -226,6 +282,8 @@ def kda_gated_norm(o, gate, weight, y, n_tokens, H, D, eps=1e-6, stream=None):
     """Head RMSNorm times sigmoid(gate); y may be o itself."""
     _same_dtype(o, gate, y)
     _f32(weight)
+    _need("kda_gated_norm", o=(o, n_tokens * H * D), gate=(gate, n_tokens * H * D),
+          y=(y, n_tokens * H * D), weight=(weight, D))
     _check("kda_gated_norm",
            lib().kda_gated_norm(_ptr(o), _ptr(gate), _ptr(weight), _ptr(y), n_tokens, H, D, eps,
                                 _dtype(o), _stream(stream)))
@@ -255,6 +313,9 @@ def kda_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, workspac
                                 dtype=torch.uint8, device=q.device)
     if scale is None:
         scale = Dk ** -0.5
+    _need("kda_mla_decode", q=(q, B * H * Dk), w_uk=(w_uk, H * Dk * R), w_uv=(w_uv, H * Dv * R),
+          cache=(cache, B * L_max * R), lengths=(lengths, B), gate=(gate, B * H * Dv),
+          y=(y, B * H * Dv))
     _check("kda_mla_decode",
            lib().kda_mla_decode(_ptr(q), _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(lengths),
                                 _ptr(gate), _ptr(y), _ptr(workspace), workspace.numel(), B, H,

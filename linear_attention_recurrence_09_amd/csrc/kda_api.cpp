@@ -5,7 +5,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "kda_launch.hpp"
 
@@ -65,6 +67,30 @@ int seq_layout(const char* fn, const int32_t* cu, int32_t num_seqs, int32_t B, i
     return KDA_OK;
 }
 
+// Debug check of packed offsets, on when the environment sets
+// KDA_CHECK_CU_SEQLENS to a value other than 0: the offsets are copied to the
+// host (this waits for the stream) and must start at 0, never decrease and
+// end at T.  The kernels clamp every sequence to [0, T] in any case, so bad
+// offsets cannot move an access out of bounds; the check reports them.
+int check_cu(const char* fn, const int32_t* cu, int num_seqs, int64_t T, hipStream_t s) {
+    const char* env = std::getenv("KDA_CHECK_CU_SEQLENS");
+    if (cu == nullptr || env == nullptr || env[0] == '\0' || env[0] == '0') return KDA_OK;
+    std::vector<int32_t> h((size_t)num_seqs + 1);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return fail(KDA_ERR_HIP, "%s: reading cu_seqlens failed", fn);
+    if (h[0] != 0) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens[0] = %d, not 0", fn, h[0]);
+    for (int i = 0; i < num_seqs; ++i)
+        if (h[i + 1] < h[i])
+            return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens decreases at %d (%d > %d)", fn, i + 1,
+                        h[i], h[i + 1]);
+    if (h[num_seqs] != T)
+        return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens[%d] = %d, T = %lld", fn, num_seqs,
+                    h[num_seqs], (long long)T);
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +112,7 @@ int kda_conv(const void* x, const float* w, void* y, const void* conv_state_in,
     int ns;
     int64_t N;
     if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (int rc = check_cu(fn, cu_seqlens, ns, N, s)) return rc;
     const int64_t P = 3LL * H * D;
     const int64_t es = esize(dtype);
     if (!aligned16(x) || !aligned16(y) || !aligned16(conv_state_in) || !aligned16(conv_state_out))
@@ -119,6 +146,7 @@ int kda_conv_mxfp8(const void* x, const float* w, void* y_codes, void* q_scale, 
     int ns;
     int64_t N;
     if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (int rc = check_cu(fn, cu_seqlens, ns, N, s)) return rc;
     const int64_t P = 3LL * H * D;
     if (!aligned16(x) || !aligned16(y_codes) || !aligned16(conv_state_in) ||
         !aligned16(conv_state_out))
@@ -174,6 +202,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, int64_t qkv_t
     int ns;
     int64_t N;
     if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (int rc = check_cu(fn, cu_seqlens, ns, N, s)) return rc;
     const kda::ChunkPlan plan = kda::plan_chunk(dtype, DK, DV, chunk, (int64_t)ns * H);
     if (!plan.ok)
         return fail(KDA_ERR_UNSUPPORTED, "%s: no variant for dtype=%d DK=%d DV=%d chunk=%d", fn,
@@ -228,6 +257,7 @@ int kda_chunk_prefill_mxfp8(const void* q, const void* q_scale, const void* k,
     int ns;
     int64_t N;
     if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (int rc = check_cu(fn, cu_seqlens, ns, N, s)) return rc;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
         !aligned16(o) || !aligned16(initial_state) || !aligned16(final_state))
         return fail(KDA_ERR_INVALID_ARG,

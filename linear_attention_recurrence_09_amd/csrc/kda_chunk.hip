@@ -35,30 +35,6 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
-// Optional stage timing (profiling builds define KDA_STAGE_PROFILE and the
-// array; workgroup 0, thread 0 records the cycles spent in each stage).
-#ifdef KDA_STAGE_PROFILE
-extern __device__ unsigned long long kda_stage_cycles[16];
-#define KDA_PROF_INIT()                                          \
-    unsigned long long prof_t_ = __builtin_readcyclecounter();  \
-    unsigned long long prof_acc_[16] = {}
-#define KDA_PROF_MARK(i)                                                  \
-    do {                                                                  \
-        const unsigned long long t_ = __builtin_readcyclecounter();      \
-        prof_acc_[i] += t_ - prof_t_;                                     \
-        prof_t_ = t_;                                                     \
-    } while (0)
-#define KDA_PROF_FLUSH()                                                  \
-    do {                                                                  \
-        if (blockIdx.x == 0 && threadIdx.x == 0)                          \
-            for (int i_ = 0; i_ < 16; ++i_) kda_stage_cycles[i_] = prof_acc_[i_]; \
-    } while (0)
-#else
-#define KDA_PROF_INIT() do {} while (0)
-#define KDA_PROF_MARK(i) do {} while (0)
-#define KDA_PROF_FLUSH() do {} while (0)
-#endif
-
 namespace kda {
 
 namespace {
@@ -275,8 +251,14 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
     const int seq = chain / H;
     const int head = chain % H;
     const int n0 = split * DVS;
-    const int64_t t_begin = cu ? (int64_t)cu[seq] : (int64_t)seq * T_len;
-    const int64_t t_end = cu ? (int64_t)cu[seq + 1] : t_begin + T_len;
+    // packed offsets are clamped to the T_len tokens of the batch, so offsets
+    // that are not monotone or exceed it never move an access out of bounds
+    int64_t t_begin = (int64_t)seq * T_len, t_end = t_begin + T_len;
+    if (cu) {
+        const int64_t a = cu[seq], b = cu[seq + 1];
+        t_begin = a < 0 ? 0 : (a > T_len ? T_len : a);
+        t_end = b < t_begin ? t_begin : (b > T_len ? T_len : b);
+    }
     const int64_t n_chunks = (t_end - t_begin + C - 1) / C;
 
     // ---- state: wave w owns key tiles [w*CTW, (w+1)*CTW) x all value tiles --
@@ -367,7 +349,6 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
         issue_loads(t_begin, (int)(len < C ? len : C));
     }
     __syncthreads();
-    KDA_PROF_INIT();
 
     for (int64_t ci = 0; ci < n_chunks; ++ci) {
         const int64_t tok0 = t_begin + ci * C;
@@ -457,15 +438,12 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             if (e < C * VROWS) *reinterpret_cast<Raw8*>(sV + (e / VROWS) * LDV + (e % VROWS) * 8) = pv[u];
         }
         if (tid < C) sBeta[tid] = to_f(pb);
-        KDA_PROF_MARK(0);
         __syncthreads();
-        KDA_PROF_MARK(7);
         // the next chunk's inputs stream in while this chunk computes
         if (ci + 1 < n_chunks) {
             const int64_t rem = t_end - (tok0 + C);
             issue_loads(tok0 + C, (int)(rem < C ? rem : C));
         }
-        KDA_PROF_MARK(1);
 
         // ================= stage 2: A_kk, A_qk tiles (MFMA) ==================
         {
@@ -485,7 +463,6 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             }
         }
         __syncthreads();
-        KDA_PROF_MARK(2);
 
         // ================= stage 3: X = (I + L)^{-1} ===========================
         // Diagonal 16x16 blocks by column-oriented forward substitution (wave b,
@@ -514,9 +491,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
 #pragma unroll
             for (int r = 0; r < 16; ++r) sL[(b0 + r) * LDL + b0 + cc] = acc[r];
         }
-        KDA_PROF_MARK(9);
         __syncthreads();
-        KDA_PROF_MARK(10);
         // Off-diagonal blocks by block rows, X_ij = -X_ii sum_{m=j}^{i-1} L_im X_mj,
         // wave j computing tile (i, j) with fp32 MFMA.  X_ij (i > j) is stored in
         // the unused upper triangle at block position (j, i), so L stays intact.
@@ -539,7 +514,6 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             }
             __syncthreads();
         }
-        KDA_PROF_MARK(3);
 
         // ================= stage 4: -W = -M'(K e^G) and Utilde = M'V ========
         // M' = X diag(beta) is formed on the fly as the A operand: row r of
@@ -610,7 +584,6 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             }
         }
         __syncthreads();   // -W complete; Kf, V, X no longer read
-        KDA_PROF_MARK(4);
 
         // ================= stage 5: U += (-W) S0,  O = (Q e^G) S0 ===========
 #pragma unroll
@@ -640,7 +613,6 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
             for (int ii = 0; ii < 4; ++ii) p[ii] = from_f<T>(accU[j][ii]);
         }
         __syncthreads();
-        KDA_PROF_MARK(5);
 
         // ================= stage 6: O += A_qk U;  S = diag(e^{G_C}) S + K^T U
 #pragma unroll
@@ -695,9 +667,7 @@ chunk_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restri
         }
         write_state_lds();
         __syncthreads();
-        KDA_PROF_MARK(6);
     }
-    KDA_PROF_FLUSH();
 
     // ---- final state ---------------------------------------------------------
     if (sT) {

@@ -26,10 +26,7 @@
 //    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  Each 16 x 16
 //    unit triangular inverse is solved by back substitution in registers
 //    (row broadcasts by DPP) by the chunk's own producer, so a chunk never
-//    waits for another producer.  (Batches of two or four chunks, solved by
-//    the batch's last producer on separate 16-lane rows, spend less VALU but
-//    couple the producers' latencies; they stay selectable.)  Results go to
-//    a ring of LDS slots.
+//    waits for another producer.  Results go to a ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
 //    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
@@ -56,45 +53,6 @@
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
-// Optional phase timing (profiling builds define KDA_PIPE_PROFILE and the
-// array): lane 0 of producer wave 0 and of consumer wave 0 in workgroup 0
-// record the cycles spent in each phase.
-#ifdef KDA_PIPE_PROFILE
-extern __device__ unsigned long long kda_pipe_cycles[16];
-#define PIPE_PROF_INIT()                                           \
-    unsigned long long pt_ = __builtin_readcyclecounter();        \
-    unsigned long long pa_[8] = {}
-#define PIPE_PROF_MARK(i)                                          \
-    do {                                                           \
-        const unsigned long long t_ = __builtin_readcyclecounter(); \
-        pa_[i] += t_ - pt_;                                        \
-        pt_ = t_;                                                  \
-    } while (0)
-#define PIPE_PROF_FLUSH(base, cond)                                            \
-    do {                                                                       \
-        if (blockIdx.x == 0 && (cond) && lane == 0)                            \
-            for (int i_ = 0; i_ < 8; ++i_) kda_pipe_cycles[(base) + i_] = pa_[i_]; \
-    } while (0)
-#define PIPE_PROF_FLUSH_CONSUMER(w)                                            \
-    do {                                                                       \
-        if (blockIdx.x == 0 && lane == 0) {                                    \
-            kda_pipe_cycles[8 + (w)] = pa_[0];                                 \
-            kda_pipe_cycles[12 + (w)] = pa_[1] + pa_[2];                       \
-        }                                                                      \
-    } while (0)
-#define PIPE_PROF_VMWAIT(i)                                                    \
-    do {                                                                       \
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                       \
-        PIPE_PROF_MARK(i);                                                     \
-    } while (0)
-#else
-#define PIPE_PROF_INIT() do {} while (0)
-#define PIPE_PROF_MARK(i) do {} while (0)
-#define PIPE_PROF_FLUSH(base, cond) do {} while (0)
-#define PIPE_PROF_FLUSH_CONSUMER(w) do {} while (0)
-#define PIPE_PROF_VMWAIT(i) do {} while (0)
-#endif
-
 namespace kda {
 
 namespace {
@@ -106,21 +64,8 @@ typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
 
 constexpr int kNP = 8;                 // producer waves (two per SIMD)
 constexpr int kRing = 8;               // LDS slots
-#ifndef KDA_PIPE_EARLY
-#define KDA_PIPE_EARLY 0                // producers do the decay arithmetic before taking the slot
-#endif
-#ifndef KDA_PIPE_BATCH
-#define KDA_PIPE_BATCH 1
-#endif
-constexpr int kBatch = KDA_PIPE_BATCH;  // chunks per triangular-inverse batch (1, 2 or 4)
-constexpr int kNBatch = kRing / kBatch; // batches in flight
 constexpr int kSpinLimit = 1 << 17;    // polls (about 128 cycles each) before giving up
-#ifndef KDA_PIPE_SLEEP
-#define KDA_PIPE_SLEEP 2                // s_sleep argument between polls (64 cycles each)
-#endif
-#ifndef KDA_PIPE_CONSUMER_PRIO
-#define KDA_PIPE_CONSUMER_PRIO 0        // wave priority of the consumer waves (0-3)
-#endif
+constexpr int kSleep = 2;              // s_sleep argument between polls (64 cycles each)
 
 template <int DK, int DVS>
 struct PipeCfg {
@@ -144,9 +89,8 @@ struct PipeCfg {
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    // triangular-inverse batches (chunks kBatch b .. kBatch b + kBatch-1,
-    // kNBatch batches in flight): per chunk the 16 columns of -N (16 floats
-    // each) and beta
+    // triangular-inverse scratch, one per slot: the 16 columns of -N (16
+    // floats each) and beta of the slot's chunk
     static constexpr int O_NB = kRing * SLOT;
     static constexpr int O_BT = O_NB + kRing * 16 * 16 * 4;
     static constexpr int BYTES = O_BT + kRing * 16 * 4;
@@ -157,8 +101,6 @@ struct PipeCfg {
     // every producer keeps one slot (rings whose size does not divide the
     // producer count gave wrong results in tests)
     static_assert(kNP % kRing == 0, "ring size divides the producer count");
-    static_assert((kBatch == 1 || kBatch == 2 || kBatch == 4) && kRing % kBatch == 0,
-                  "inverse batches cover the ring");
 };
 
 // Position of channel c inside its 32-channel group in the permuted tiles:
@@ -199,7 +141,7 @@ __device__ __forceinline__ float row_bcast(float x) {
 }
 // y += (lane M of the row's n) * m, one v_fmac_f32 with a DPP row broadcast
 // on its first source.  The broadcast operand must not be written by a VALU
-// instruction in the two instructions before (see back_subst).
+// instruction in the two instructions before (see back_subst_split).
 template <int M>
 __device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
     asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
@@ -207,37 +149,18 @@ __device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
                  : "v"(n), "v"(m), "i"(M));
 }
 
-template <int M>
-__device__ __forceinline__ void back_subst_steps(float (&y)[16], const float (&np)[16]) {
-    if constexpr (M >= 1) {
-#pragma unroll
-        for (int r = 0; r < M; ++r) fmac_bcast<M>(y[r], np[r], y[M]);
-        back_subst_steps<M - 1>(y, np);
-    }
-}
-
-// Back substitution for Y = (I + N)^{-1}, N strictly upper triangular, in a
-// column layout replicated over the four rows: lane c of every row holds
-// column c of -N in np[0..15] and builds column c of Y - I in y[0..15].
-// With y started at np, Y - I = -N + (-N)(Y - I) is solved column-oriented:
-// entry M of y is final once the entries above it are done, and it updates
-// every row r < M with -N[r][M], taken from lane M of the row.  np is complete
-// before the first broadcast read (the s_nop consumes it and adds the DPP read
-// wait states).
-__device__ __forceinline__ void back_subst(float (&y)[16], const float (&np)[16]) {
-    asm volatile("s_nop 1" ::"v"(np[0]), "v"(np[1]), "v"(np[2]), "v"(np[3]), "v"(np[4]),
-                 "v"(np[5]), "v"(np[6]), "v"(np[7]), "v"(np[8]), "v"(np[9]), "v"(np[10]),
-                 "v"(np[11]), "v"(np[12]), "v"(np[13]), "v"(np[14]));
-    back_subst_steps<15>(y, np);
-}
-
-// The same solve split over the four 16-lane rows (one chunk per wave): lane
-// c of row q holds rows r = q + 4k (k = 0..3) of column c, of -N in np[k] and
+// Back substitution for Y = (I + N)^{-1}, N strictly upper triangular, split
+// over the four 16-lane rows (one chunk per wave): with Y - I = -N - N(Y - I)
+// solved column by column, entry M of a column is final once the entries
+// above it are done, and it updates every row r < M with -N[r][M].  Lane c
+// of row q holds rows r = q + 4k (k = 0..3) of column c, of -N in np[k] and
 // of Y in y[k] (started at column c of I, so Y comes out with its diagonal).
 // Step M fetches the finished entry Y[M][c] from its owner row (M % 4, slot
 // M / 4; one ds_bpermute) and updates the slots k < ceil(M / 4) of every row:
 // the rows r >= M among them add -N[r][M] = 0 (the masked entries are stored
-// as zeros).  36 broadcast multiply-adds instead of 120.
+// as zeros).  36 broadcast multiply-adds in all.  np is complete before the
+// first broadcast read (the s_nop consumes it and adds the DPP read wait
+// states).
 template <int M>
 __device__ __forceinline__ void back_subst_split_steps(float (&y)[4], const float (&np)[4],
                                                        int lr) {
@@ -282,17 +205,11 @@ __device__ __forceinline__ int flag_load(int* f) {
 __device__ __forceinline__ void flag_store(int* f, int v, int lane) {
     if (lane == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Count a chunk into its inverse batch: returns the count before this one
-// (wave-uniform).  Release: this wave's LDS writes are done before the count;
-// acquire: the wave that counts last sees every writer of the batch.
-__device__ __forceinline__ int batch_count(int* c, int lane) {
-    int v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return __builtin_amdgcn_readfirstlane(v);
-}
-
-// Wait until all N counters f[0..N-1] are >= target (N = 4).  Returns false (and raises the workgroup's stop flag) if the wait runs
-// out, or if another wave has raised it.
+// Wait until all N counters f[0..N-1] are >= target (N = 4).  Returns false
+// (and raises the workgroup's stop flag) if the wait runs out, or if another
+// wave has raised it.  The polls are relaxed (four loads in flight at once);
+// the acquire fence after the poll that succeeds pairs with the consumers'
+// releases, so the slot writes that follow stay behind it.
 template <int N>
 __device__ __forceinline__ bool wait_all_at_least(int* f, int target, int* stop) {
     static_assert(N == 4, "four consumer counters");
@@ -313,11 +230,9 @@ __device__ __forceinline__ bool wait_all_at_least(int* f, int target, int* stop)
             __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
         }
-        __builtin_amdgcn_s_sleep(KDA_PIPE_SLEEP);
+        __builtin_amdgcn_s_sleep(kSleep);
     }
-    // the slot is written only after the counters were seen (the LDS serves
-    // a wave's operations in order; the compiler keeps the writes below)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     return true;
 }
 
@@ -333,7 +248,7 @@ __device__ __forceinline__ bool wait_at_least(int* f, int target, int* stop) {
             __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             return false;
         }
-        __builtin_amdgcn_s_sleep(KDA_PIPE_SLEEP);
+        __builtin_amdgcn_s_sleep(kSleep);
     }
     return true;
 }
@@ -382,14 +297,12 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
-    // ready[kRing], released[kRing][NC] (one counter per consumer), stop,
-    // batch[kNBatch] (chunks counted into the inverse batches in flight)
-    constexpr int NFLAGS = kRing + kRing * NC + 1 + kNBatch;
+    // ready[kRing], released[kRing][NC] (one counter per consumer), stop
+    constexpr int NFLAGS = kRing + kRing * NC + 1;
     __shared__ __attribute__((aligned(16))) int flags[NFLAGS];
     int* ready = flags;
     int* released = flags + kRing;
     int* stop = flags + kRing + kRing * NC;
-    int* batch = stop + 1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -417,8 +330,14 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int seq = chain / H;
     const int head = chain % H;
     const int n0 = split * DVS;
-    const int64_t t_begin = cu ? (int64_t)cu[seq] : (int64_t)seq * T_len;
-    const int64_t t_end = cu ? (int64_t)cu[seq + 1] : t_begin + T_len;
+    // packed offsets are clamped to the T_len tokens of the batch, so offsets
+    // that are not monotone or exceed it never move an access out of bounds
+    int64_t t_begin = (int64_t)seq * T_len, t_end = t_begin + T_len;
+    if (cu) {
+        const int64_t a = cu[seq], b = cu[seq + 1];
+        t_begin = a < 0 ? 0 : (a > T_len ? T_len : a);
+        t_end = b < t_begin ? t_begin : (b > T_len ? T_len : b);
+    }
     const int64_t n_chunks = (t_end - t_begin + 15) / 16;
     const int nch = (int)n_chunks;
 
@@ -517,7 +436,6 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         };
         issue_gkq(pw);
         issue_v(pw);
-        PIPE_PROF_INIT();
 
         // The loop has no early exit: an exit path would merge with the
         // prefetch registers at the loop's latch and make every iteration wait
@@ -528,9 +446,7 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         for (int64_t ci = pw; ci < n_chunks;) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
-            PIPE_PROF_VMWAIT(5);
-            bool go = true;
-            if (!KDA_PIPE_EARLY) go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+            const bool go = wait_all_at_least<NC>(&released[s * NC], round, stop);
 
             // ---- decay products, in registers -------------------------------
             // a_t = e^{g_t}; F_t = e^{G_t} = a_0 .. a_t (forward), then
@@ -581,23 +497,8 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             // add a register move that waits for the loads)
             float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
             asm volatile("" : "+v"(bl));
-            // with the arithmetic ahead of the wait, the tile words are
-            // computed here (the compiler would otherwise sink it to the stores)
-            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wkt[0]), "v"(wkt[1]), "v"(wkt[2]), "v"(wkt[3]), "v"(wkt[4]), "v"(wkt[5]),
-                         "v"(wkt[6]), "v"(wkt[7]), "v"(wkt[8]), "v"(wkt[9]), "v"(wkt[10]), "v"(wkt[11]),
-                         "v"(wkt[12]), "v"(wkt[13]), "v"(wkt[14]), "v"(wkt[15]));
-            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wqt[0]), "v"(wqt[1]), "v"(wqt[2]), "v"(wqt[3]), "v"(wqt[4]), "v"(wqt[5]),
-                         "v"(wqt[6]), "v"(wqt[7]), "v"(wqt[8]), "v"(wqt[9]), "v"(wqt[10]), "v"(wqt[11]),
-                         "v"(wqt[12]), "v"(wqt[13]), "v"(wqt[14]), "v"(wqt[15]));
-            if (KDA_PIPE_EARLY) asm volatile("" ::"v"(wki[0]), "v"(wki[1]), "v"(wki[2]), "v"(wki[3]), "v"(wki[4]), "v"(wki[5]),
-                         "v"(wki[6]), "v"(wki[7]), "v"(wki[8]), "v"(wki[9]), "v"(wki[10]), "v"(wki[11]),
-                         "v"(wki[12]), "v"(wki[13]), "v"(wki[14]), "v"(wki[15]), "v"(F[0]), "v"(F[CPL - 1]));
-            PIPE_PROF_MARK(1);
-
             // ---- into the slot -----------------------------------------------
-            if (KDA_PIPE_EARLY) go = wait_all_at_least<NC>(&released[s * NC], round, stop);
             char* slot = smem + s * SLOT;
-            PIPE_PROF_MARK(0);
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
@@ -632,7 +533,6 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             // the next chunk of this wave streams in from here on
             issue_gkq(ci + kNP);
             issue_v(ci + kNP);
-            PIPE_PROF_MARK(2);
 
             // ---- A_kk^T, A_qk^T (16x16x32 MFMA over the key channels) -------
             floatx4 akk = zero4(), aqk = zero4();
@@ -654,107 +554,46 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             *reinterpret_cast<shortx4*>(slot + Cfg::O_AQ + lane * 8) =
                 pack4(4 * lq + 0 <= lr ? aqk[0] : 0.f, 4 * lq + 1 <= lr ? aqk[1] : 0.f,
                       4 * lq + 2 <= lr ? aqk[2] : 0.f, 4 * lq + 3 <= lr ? aqk[3] : 0.f);
-            PIPE_PROF_MARK(3);
 
-            // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk, in batches ------------
-            // This chunk's part: column c = lr of -N holds -beta_c A_kk[c][r]
-            // for r < c; lane (q, c) has rows r = 4q+i (the tile holds -Kt, so
-            // akk[i] = -A_kk[c][4q+i]).  It goes through LDS, with beta (to the
-            // column layout of the solve), and the last chunk of its batch to
-            // get here inverts the whole batch -- with one chunk per batch, this
-            // wave, right away -- one chunk per 4/kBatch of the 16-lane rows
-            // (the row broadcasts of the back substitution stay inside a row).
-            constexpr int RPC = 4 / kBatch;   // lane rows per chunk
-            const int cix = (int)ci;
-            const int bt = cix / kBatch, bslot = bt % kNBatch;
-            float* nbp = reinterpret_cast<float*>(smem + Cfg::O_NB);
-            float* btp = reinterpret_cast<float*>(smem + Cfg::O_BT);
-            const int mine = bslot * kBatch + cix % kBatch;   // this chunk's buffer
-            *reinterpret_cast<floatx4*>(nbp + (mine * 16 + lr) * 16 + 4 * lq) =
+            // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk ------------------------
+            // Column c = lr of -N holds -beta_c A_kk[c][r] for r < c; lane
+            // (q, c) has rows r = 4q+i (the tile holds -Kt, so akk[i] =
+            // -A_kk[c][4q+i]).  It goes through this slot's scratch, with beta,
+            // to the column layout of the solve, which the four lane rows share
+            // (see back_subst_split); each row then writes its rows of M'.
+            float* col = reinterpret_cast<float*>(smem + Cfg::O_NB) + (s * 16 + lr) * 16;
+            float* bet = reinterpret_cast<float*>(smem + Cfg::O_BT) + s * 16;
+            *reinterpret_cast<floatx4*>(col + 4 * lq) =
                 floatx4{4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
                         4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
-            if (lq == 0) btp[mine * 16 + lr] = bl;
-            // chunks of the batch, and the count of this buffer's earlier
-            // batches (all full: only the last batch can be short)
-            const int n_in = nch - kBatch * bt < kBatch ? nch - kBatch * bt : kBatch;
-            const int counted = go ? batch_count(&batch[bslot], lane) : -1;
-            if constexpr (kBatch == 1) {
-                // one chunk: the four lane rows share its solve (see
-                // back_subst_split) and each writes its rows of M'
-                if (counted == bt / kNBatch) {
-                    const float* col = nbp + (mine * 16 + lr) * 16;
-                    const float* bet = btp + mine * 16;
-                    float np[4], y[4];
+            if (lq == 0) bet[lr] = bl;
+            if (go) {
+                float np[4], y[4];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        np[k] = col[lq + 4 * k];
-                        y[k] = lq + 4 * k == lr ? 1.f : 0.f;
-                    }
-                    back_subst_split(y, np, lr);
-                    // M'[lr][4k+q] = Y[4k+q][lr] beta_{4k+q}: entry q of the
-                    // 4-entry group k of lane (k, lr) of the 16x16x16 A operand
-                    char* slot_g = smem + (cix % kRing) * SLOT;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        *reinterpret_cast<__bf16*>(slot_g + Cfg::O_MP + (16 * k + lr) * 8 + lq * 2) =
-                            (__bf16)(y[k] * bet[4 * k + lq]);
-                    // publish the chunk after every lane's M' writes (the
-                    // release waits for them)
-                    if (lq == 0 && lr == 0)
-                        __hip_atomic_store(&ready[cix % kRing], cix / kRing + 1, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+                for (int k = 0; k < 4; ++k) {
+                    np[k] = col[lq + 4 * k];
+                    y[k] = lq + 4 * k == lr ? 1.f : 0.f;
                 }
-            } else if (counted == kBatch * (bt / kNBatch) + n_in - 1) {
-                // lane (row, c): chunk kBatch bt + row / RPC, column c of -N,
-                // then of Y - I
-                const int gi = lq / RPC;
-                float np[16], y[16];
-                const float* col = nbp + ((bslot * kBatch + gi) * 16 + lr) * 16;
+                back_subst_split(y, np, lr);
+                // M'[lr][4k+q] = Y[4k+q][lr] beta_{4k+q}: entry q of the
+                // 4-entry group k of lane (k, lr) of the 16x16x16 A operand
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const floatx4 v4 = *reinterpret_cast<const floatx4*>(col + 4 * j);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) np[4 * j + e] = v4[e];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] = np[r];
-                back_subst(y, np);
-                // M'[r][4q+e] = Y[4q+e][r] beta_{4q+e}, lane (q, r) of the
-                // chunk's 16x16x16 A operand; this lane holds column r = lr of
-                // Y - I (the first lane row of each chunk writes it)
-                const int cg = kBatch * bt + gi;
-                const bool writer = lq % RPC == 0 && gi < n_in;
-                if (writer) {
-                    char* slot_g = smem + (cg % kRing) * SLOT;
-                    const float* bet = btp + (bslot * kBatch + gi) * 16;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const floatx4 bq = *reinterpret_cast<const floatx4*>(bet + 4 * q4);
-                        *reinterpret_cast<shortx4*>(slot_g + Cfg::O_MP + (16 * q4 + lr) * 8) =
-                            pack4(y[4 * q4] * bq[0], y[4 * q4 + 1] * bq[1], y[4 * q4 + 2] * bq[2],
-                                  y[4 * q4 + 3] * bq[3]);
-                    }
-                    // the unit diagonal: entry lr of y is exactly 0 (a column
-                    // of Y - I has nothing on or below the diagonal), so
-                    // M'[lr][lr] = beta_lr goes in with one 2-byte write
-                    *reinterpret_cast<__bf16*>(slot_g + Cfg::O_MP + (16 * (lr >> 2) + lr) * 8 + (lr & 3) * 2) =
-                        (__bf16)bet[lr];
-                }
-                // publish the batch's chunks, one lane per chunk, after the
-                // M' writes (the release waits for them)
-                if (writer && lr == 0)
-                    __hip_atomic_store(&ready[cg % kRing], cg / kRing + 1, __ATOMIC_RELEASE,
+                for (int k = 0; k < 4; ++k)
+                    *reinterpret_cast<__bf16*>(slot + Cfg::O_MP + (16 * k + lr) * 8 + lq * 2) =
+                        (__bf16)(y[k] * bet[4 * k + lq]);
+                // publish the chunk after every lane's M' writes (the LDS
+                // performs this wave's operations in order; the release keeps
+                // the compiler from sinking the writes below it)
+                if (lane == 0)
+                    __hip_atomic_store(&ready[s], round + 1, __ATOMIC_RELEASE,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            PIPE_PROF_MARK(4);
             ci = go ? ci + kNP : n_chunks;
         }
-        PIPE_PROF_FLUSH(0, pw == 0);
         return;
     }
 
     // ======================== consumer wave ==================================
-    if (KDA_PIPE_CONSUMER_PRIO > 0) __builtin_amdgcn_s_setprio(KDA_PIPE_CONSUMER_PRIO);
     const int w = wave;                      // value columns n0 + 16w .. +15
     floatx4 S[NKT];
     const int64_t sbase = ((int64_t)seq * H + head) * DK * DV + n0 + 16 * w + lr;
@@ -804,7 +643,6 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int o_row = H * DV * 2;   // bytes between tokens
     const __bf16* o_chunk = o + (t_begin * H + head) * DV + n0 + 16 * w;
     int rows_left = (int)(t_end - t_begin);
-    PIPE_PROF_INIT();
     for (unsigned ci = ok ? 0u : (unsigned)nch; ci < (unsigned)nch;) {
         const char* slot = smem + (ci % kRing) * SLOT;
         // the rest of this chunk's operands
@@ -814,12 +652,13 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         const shortx4 aq = *reinterpret_cast<const shortx4*>(slot + Cfg::O_AQ + lane * 8);
         const floatx2 gm = *reinterpret_cast<const floatx2*>(slot + Cfg::O_GM + (lq * 16 + lr) * 8);
         // the next chunk's counter, read early (a value already at the target
-        // saves the polling round trip later)
+        // saves the polling round trip later); the acquire that pairs with the
+        // producer's release is the fence below, once the value is used, so
+        // the products need not wait for this chunk's operand reads
         const unsigned cn = ci + 1;
         int* rdy = &ready[cn % kRing];
         const int target = cn < (unsigned)nch ? (int)(cn / kRing) + 1 : 0;
         const int peek = __hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        PIPE_PROF_MARK(0);
 
         // S as permuted bf16 operands: the same registers are the B operand of
         // S and the A operand of S^T
@@ -855,13 +694,13 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         flag_store(&released[(ci % kRing) * NC + w], (int)(ci / kRing) + 1, lane);
         // the next chunk's leading operands, read while the state updates
         ok = __builtin_amdgcn_readfirstlane(peek) >= target || wait_at_least(rdy, target, stop);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         asm volatile("" ::"s"((int)ok) : "memory");
         read_head(smem + (cn % kRing) * SLOT);
         // S <- diag(e^{G_15}) (S + Ki^T U): row i of tile kt is channel
         // 16 kt + 4q + i; its decay sits in lane 2 kt + i/2 of the lane's own
         // row, component i % 2
         decay_rows<0, NKT>(S, gm);
-        PIPE_PROF_MARK(1);
 
         // lane (q, t) holds O[t][16w + 4q .. +3]: one 8-byte store per lane;
         // the resource covers the chunk's rows inside the sequence, so rows
@@ -872,10 +711,8 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             lr * o_row + 8 * lq, 0, 0);
         o_chunk += 16 * H * DV;
         rows_left -= 16;
-        PIPE_PROF_MARK(2);
         ci = ok ? cn : (unsigned)nch;
     }
-    PIPE_PROF_FLUSH_CONSUMER(w);
     if (sT != nullptr) {
         const float nan = __builtin_nanf("");
 #pragma unroll

@@ -55,9 +55,20 @@ struct SeqRange {
     int64_t start, end;
 };
 
+// Token range [start, end) of packed sequence s, clamped to the N tokens of
+// the batch (0 <= start <= end <= N), so offsets that are not monotone or
+// exceed N never move an access out of bounds.
+__device__ __forceinline__ void seq_bounds(const int32_t* cu, int s, int64_t N, int64_t& start,
+                                           int64_t& end) {
+    const int64_t a = cu[s], b = cu[s + 1];
+    start = a < 0 ? 0 : (a > N ? N : a);
+    end = b < start ? start : (b > N ? N : b);
+}
+
 // Sequence holding token t: the largest s with start(s) <= t (empty
 // sequences are skipped because their successor starts at the same token).
-__device__ __forceinline__ SeqRange find_seq(const int32_t* cu, int num_seqs, int T, int64_t t) {
+__device__ __forceinline__ SeqRange find_seq(const int32_t* cu, int num_seqs, int T, int64_t N,
+                                             int64_t t) {
     SeqRange r;
     if (cu == nullptr) {
         r.s = (int)(t / T);
@@ -71,8 +82,7 @@ __device__ __forceinline__ SeqRange find_seq(const int32_t* cu, int num_seqs, in
         if (cu[mid] <= t) lo = mid; else hi = mid - 1;
     }
     r.s = lo;
-    r.start = cu[lo];
-    r.end = cu[lo + 1];
+    seq_bounds(cu, lo, N, r.start, r.end);
     return r;
 }
 
@@ -221,7 +231,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) wt[e][i] = active ? w[(c0 + e) * 4 + i] : 0.f;
 
-    SeqRange sr = find_seq(cu, num_seqs, T_len, t0);
+    SeqRange sr = find_seq(cu, num_seqs, T_len, N, t0);
 
     // Fast path (uniform over the block): the strip and its halo lie inside one
     // sequence, so every window reads plain inputs.
@@ -314,8 +324,7 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
                     sr.end = sr.start + T_len;
                 } else if (sr.s + 1 < num_seqs) {
                     sr.s += 1;
-                    sr.start = cu[sr.s];
-                    sr.end = cu[sr.s + 1];
+                    seq_bounds(cu, sr.s, N, sr.start, sr.end);
                 } else {
                     sr.end = t1;         // offsets inconsistent with N: stay in bounds
                 }
@@ -346,12 +355,13 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
 template <typename T>
 __global__ void __launch_bounds__(kConvThreads)
 conv_state_kernel(const T* __restrict__ x, const T* state_in, T* state_out,
-                  const int32_t* __restrict__ cu, int T_len, int P) {
+                  const int32_t* __restrict__ cu, int T_len, int64_t N, int P) {
     const int s = blockIdx.x;
     const int c0 = blockIdx.y * kConvChannels + threadIdx.x * 8;
     if (c0 >= P) return;
-    const int64_t start = cu ? (int64_t)cu[s] : (int64_t)s * T_len;
-    const int64_t len = cu ? (int64_t)cu[s + 1] - start : (int64_t)T_len;
+    int64_t start = (int64_t)s * T_len, end = start + T_len;
+    if (cu) seq_bounds(cu, s, N, start, end);
+    const int64_t len = end - start;
     float st[8][3];
     load_state8(state_in, s, P, c0, st);
     float v[24];
@@ -399,7 +409,7 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
         const unsigned sblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
         hipLaunchKernelGGL((conv_state_kernel<T>), dim3((unsigned)num_seqs, sblocks),
                            dim3(kConvThreads), 0, s, (const T*)x, (const T*)state_in,
-                           (T*)state_out, cu, T_len, P);
+                           (T*)state_out, cu, T_len, N, P);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -22,29 +22,17 @@ namespace kda {
 
 namespace {
 
-#ifndef KDA_DECODE_THREADS
-#define KDA_DECODE_THREADS 256
-#endif
-#ifndef KDA_DECODE_NONTEMPORAL
-#define KDA_DECODE_NONTEMPORAL 1
-#endif
-constexpr int kDecThreads = KDA_DECODE_THREADS;
+constexpr int kDecThreads = 256;
 
+// The state streams through once per call: non-temporal loads and stores keep
+// it from displacing cached data.
 template <typename V>
 __device__ __forceinline__ V stream_load(const V* p) {
-#if KDA_DECODE_NONTEMPORAL
     return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
 }
 template <typename V>
 __device__ __forceinline__ void stream_store(V v, V* p) {
-#if KDA_DECODE_NONTEMPORAL
     __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
 }
 
 // Several new tokens per sequence in one pass over the state: the K tokens a
