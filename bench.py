@@ -277,10 +277,50 @@ def bench_mxfp8_prefill(kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D
             "kernels_hbm_frac": {k: nb[k] / (km[k] * 1e-3) / 1e9 / HBM_PEAK_GBS for k in km}}
 
 
-def cpu_baseline(inp, spec, T_s, H_s):
-    """Oracle on the first T_s tokens of the first H_s heads (all its threads)."""
+def _cpu_info():
+    """Host CPU model, nominal clock and the threads this process may use."""
+    model, mhz = "unknown", None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name") and model == "unknown":
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("cpu MHz") and mhz is None:
+                    mhz = float(line.split(":", 1)[1])
+    except (OSError, ValueError):
+        pass
+    return {"cpu_model": model, "cpu_mhz": mhz, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def parity_figures(gpu, ref, block=16):
+    """rel-L2, the largest rel-L2 over blocks of `block` rows of the leading
+    (token) axis, max-abs and max-abs over the reference's RMS."""
     import numpy as np
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    d = g - r
+    rn = float(np.linalg.norm(r))
+    rms = rn / np.sqrt(r.size)
+    rows = r.shape[0]
+    nb = rows // block
+    worst = 0.0
+    if nb:
+        bd = np.sqrt(np.square(d[:nb * block]).reshape(nb, -1).sum(axis=1))
+        br = np.sqrt(np.square(r[:nb * block]).reshape(nb, -1).sum(axis=1))
+        floor = 0.25 * rms * np.sqrt(r[:block].size)
+        worst = float((bd / np.maximum(br, floor)).max())
+    ma = float(np.abs(d).max())
+    return {"rel_l2": float(np.linalg.norm(d) / rn), "max_block_rel_l2": worst,
+            "max_abs": ma, "max_abs_over_rms": ma / rms}
+
+
+def cpu_baseline(inp, spec, T_s, H_s, gpu_out):
+    """The CPU oracle on the first T_s tokens of the first H_s heads (all its
+    threads), plus one-thread figures on the tiny workload and on a sample of
+    the T = 4,096 workload; and the parity of the timed GPU step's outputs
+    (o, y, final state) on the same heads against that oracle run."""
     import torch
+    import synth
     from oracle import c_oracle
     nthr = c_oracle.num_threads()
     H_s = min(H_s, spec.H)
@@ -297,21 +337,48 @@ def cpu_baseline(inp, spec, T_s, H_s):
     gs, bs, zs = f(inp["g"][:T_s, heads]), f(inp["beta"][:T_s, heads]), f(inp["gate"][:T_s, heads])
     nw = f(inp["norm_w"])
     t0 = time.perf_counter()
-    c_oracle.kda_prefill(xs, ws, gs, bs, zs, nw, [0, T_s], H_s, D)
+    ref = c_oracle.kda_prefill(xs, ws, gs, bs, zs, nw, [0, T_s], H_s, D)
     dt = time.perf_counter() - t0
-    del np
-    cpu = "unknown"
+    del xs, gs, bs, zs
+    parity = {"workload": f"the timed step's outputs, heads 0..{H_s - 1} of {H}, tokens 0.."
+                          f"{T_s - 1}, against the C fp64 oracle (bar: 2e-2 for rel-L2 and "
+                          f"for every 16-token block)"}
+    for key in ("o", "y"):
+        parity[key] = parity_figures(f(gpu_out[key][:T_s, heads]), ref[key])
+    if T_s == gpu_out["o"].shape[0]:
+        parity["S_final"] = parity_figures(f(gpu_out["S_final"][:, heads]), ref["S_final"])
+    del ref
+    # one host thread: the tiny workload whole, and 2 heads of T = 4,096
+    one = {}
+    c_oracle.set_num_threads(1)
     try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
-                       cpu)
-    except OSError:
-        pass
-    return {"value": T_s * H_s / H / dt, "unit": "tokens/s", "cores": min(nthr, H_s),
-            "kind": "oracle", "cpu_model": cpu,
+        for cid, nh in ((0, None), (1, 2)):
+            es = synth.CONFIGS[cid]
+            ei = synth.prefill_inputs(es, device="cpu")
+            hs = list(range(es.H if nh is None else nh))
+            cc = []
+            for part in range(3):
+                for h in hs:
+                    cc.extend(range(part * es.H * es.D + h * es.D, part * es.H * es.D + (h + 1) * es.D))
+            cc = torch.as_tensor(cc)
+            a = [f(ei["x"].index_select(1, cc)), f(ei["conv_w"].index_select(0, cc)),
+                 f(ei["g"][:, hs]), f(ei["beta"][:, hs]), f(ei["gate"][:, hs]), f(ei["norm_w"])]
+            t1 = time.perf_counter()
+            c_oracle.kda_prefill(*a, ei["cu"], len(hs), es.D)
+            d1 = time.perf_counter() - t1
+            Ne = ei["x"].shape[0]
+            one[es.name] = {"seconds": d1, "heads_run": len(hs), "heads": es.H,
+                            "tokens_per_s": Ne * len(hs) / es.H / d1, "cores": 1}
+    finally:
+        c_oracle.set_num_threads(nthr)
+    base = {"value": T_s * H_s / H / dt, "unit": "tokens/s", "cores": min(nthr, H_s),
+            "kind": "oracle", **_cpu_info(), "head_scale": H_s / H,
             "sample": (f"C fp64 oracle, whole prefill path (conv, L2, recurrence, gated norm) on "
-                       f"the first {T_s} tokens of {H_s} of the {H} heads, {dt:.1f} s; "
-                       f"scaled to tokens/s of the {H}-head layer")}
+                       f"the first {T_s} tokens of {H_s} of the {H} heads, {dt:.1f} s on "
+                       f"{min(nthr, H_s)} threads; value = tokens/s of the {H}-head layer "
+                       f"= {T_s} x {H_s}/{H} / {dt:.1f} s"),
+            "one_thread": one}
+    return base, parity
 
 
 def main():
@@ -472,6 +539,7 @@ def main():
     # the other two prefill workloads, timed the same way (informative: the
     # headline value is the workload above)
     extra = {}
+    flush = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
     for cid in (1, 3):
         es = synth.CONFIGS[cid]
         ei = synth.prefill_inputs(es, device="cuda")
@@ -505,16 +573,19 @@ def main():
         eev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
+            flush.fill_(float(i))      # 512 MB written between repetitions (caches flushed)
             estep(eev[i])
         torch.cuda.synchronize()
         km = {n: sum(e[j].elapsed_time(e[j + 1]) for e in eev) / args.steps
               for j, n in enumerate(("conv", "chunk", "norm"))}
         ms = sum(km.values())
         extra[es.name] = {"tokens": Ne, "sequences": Se, "ms_per_step": ms,
-                          "tokens_per_s": Ne / (ms * 1e-3), "kernels_ms": km}
+                          "tokens_per_s": Ne / (ms * 1e-3), "kernels_ms": km,
+                          "timing": "kernel events; a 512 MB buffer written before each step"}
         log(f"{es.name}: {ms:.3f} ms/step, {Ne / ms / 1e3:.2f} M tokens/s")
         del ei, ye, oe, yn, sTe
     result["prefill_other_workloads"] = extra
+    del flush
 
     if not args.no_decode:
         dspec = synth.CONFIGS[4]
@@ -625,8 +696,10 @@ def main():
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_tokens, args.cpu_heads)
-        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            inp, spec, args.cpu_tokens, args.cpu_heads, {"o": o, "y": y, "S_final": sT})
+        log(f"cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s; parity "
+            f"{json.dumps(result['parity'])}")
     # the 1M-token regime: the chunk kernel alone over one sequence of
     # 1,048,576 tokens at 96 x 128 (129 GB of device buffers, filled in place
     # in bf16 with the value ranges of the workloads above)

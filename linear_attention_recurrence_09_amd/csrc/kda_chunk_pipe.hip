@@ -310,8 +310,12 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int lr = lane & 15;
     const int lq = lane >> 4;
 
-    // ---- workgroup -> (sequence, head, value slice); slices of one chain are
-    // placed 8 ids apart so they run on the same XCD and share its L2 --------
+    // ---- workgroup -> (sequence, head, value slice).  Workgroups are dealt to
+    // the 8 XCDs in turn (ids x, x+8, ... run on XCD x), so XCD x is given a
+    // contiguous run of chains: the value slices of a chain sit 8 ids apart
+    // on one XCD, and a token's beta and block-scale bytes for that XCD's
+    // heads are one short contiguous range of its row, fetched into its L2
+    // once instead of every XCD fetching the whole row ---------------------
     const int nchain = num_seqs * H;
     const int total = nchain * nsplit;
     const int bid = blockIdx.x;
@@ -319,9 +323,9 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int full = (total / span) * span;
     int chain, split;
     if (bid < full) {
-        const int gi = bid >> 3, xcd = bid & 7;
-        chain = (gi / nsplit) * 8 + xcd;
-        split = gi % nsplit;
+        const int j = bid >> 3, xcd = bid & 7;
+        chain = xcd * (full / span) + j / nsplit;
+        split = j % nsplit;
     } else {
         const int r = bid - full;
         chain = full / nsplit + r / nsplit;

@@ -29,6 +29,7 @@ def lib():
                                             dp, dp, d, d, dp, dp, dp, i64, lp, dp]
         _lib.oracle_kda_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, d]
         _lib.oracle_num_threads.restype = ctypes.c_int
+        _lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return _lib
 
 
@@ -50,6 +51,10 @@ def _pl(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
 
 
 def short_conv_silu(x, w, state_in=None):

@@ -39,6 +39,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops that follow (timing runs on one core). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------------------
  * [CONV] Causal depthwise convolution of width 4 followed by SiLU.
  *

@@ -8,7 +8,7 @@ import torch
 
 import linear_attention_recurrence_09_amd as kda
 from oracle import c_oracle, kda_ref
-from tests.kda_testlib import TOL, f64, max_abs, rel_l2, report
+from tests.kda_testlib import ELEM, TOL, f64, max_abs, rel_l2, report
 
 pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -38,7 +38,7 @@ def test_gated_norm(dtype, D, n):
     y = torch.empty_like(o)
     kda.kda_gated_norm(o, z, w, y, n, H, D)
     ref = c_oracle.gated_rmsnorm(f64(o), f64(z), f64(w))
-    assert report("y", f64(y), ref, TOL[dtype]) <= TOL[dtype]
+    assert report("y", f64(y), ref, TOL[dtype], elem=ELEM[dtype]) <= TOL[dtype]
     kda.kda_gated_norm(o, z, w, o, n, H, D)             # in place
     torch.cuda.synchronize()
     assert torch.equal(o, y)
@@ -84,7 +84,7 @@ def test_conv(case):
         ys[:, :2] = kda_ref.l2norm(ys[:, :2])
         ref_y[t0:t1] = ys.reshape(t1 - t0, P)
     if N:
-        assert report("y", f64(y), ref_y, TOL[dtype]) <= TOL[dtype]
+        assert report("y", f64(y), ref_y, TOL[dtype], elem=ELEM[dtype]) <= TOL[dtype]
     assert np.array_equal(f64(so), ref_s)
     # in-place rolling state gives the same result
     if si is not None:
