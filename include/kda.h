@@ -293,6 +293,31 @@ int kda_mla_decode(const void* q, const void* w_uk, const void* w_uv, const void
                    int64_t workspace_bytes, int32_t B, int32_t H, int32_t L_max, int32_t R,
                    int32_t Dk, int32_t Dv, float scale, int32_t dtype, hipStream_t s);
 
+/*
+ * kda_mla_decode_noalloc -- kda_mla_decode for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, bitwise the same y, with the
+ * workspace replaced by a static device array of the library of
+ * KDA_MLA_NOALLOC_MAX_BYTES (128 MiB), which each GPU that runs the library
+ * holds until the process ends.  Arguments, layouts and checks are those of
+ * kda_mla_decode without `workspace` / `workspace_bytes`.
+ *
+ * - A call whose kda_mla_decode_workspace_bytes(B, H, L_max) exceeds
+ *   KDA_MLA_NOALLOC_MAX_BYTES returns KDA_ERR_INVALID_ARG and launches
+ *   nothing (B = 256, H = 96 needs about 75 MiB at any L_max; every B <= 256
+ *   with H <= 96 fits).
+ * - Nothing is allocated: the array's device address is looked up once per
+ *   device, on the first call with that device current.
+ * - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents (no call depends on them).  Calls that overlap in time on one
+ *   GPU (other streams, other threads) race on it: serialise them.
+ */
+#define KDA_MLA_NOALLOC_MAX_BYTES (128LL << 20)
+int kda_mla_decode_noalloc(const void* q, const void* w_uk, const void* w_uv, const void* cache,
+                           const int32_t* lengths, const void* gate, void* y, int32_t B,
+                           int32_t H, int32_t L_max, int32_t R, int32_t Dk, int32_t Dv,
+                           float scale, int32_t dtype, hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,11 +13,13 @@ import torch
 
 __all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
            "kda_decode_step", "kda_decode_multi", "kda_gated_norm", "kda_prefill",
-           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_chunk_prefill_mxfp8", "kda_conv_mxfp8",
+           "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_mla_decode_noalloc",
+           "kda_chunk_prefill_mxfp8", "kda_conv_mxfp8", "KDA_MLA_NOALLOC_MAX_BYTES",
            "KDA_F32",
            "KDA_BF16"]
 
 KDA_F32, KDA_BF16 = 0, 1
+KDA_MLA_NOALLOC_MAX_BYTES = 128 << 20      # the static scratch of kda_mla_decode_noalloc
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
@@ -56,9 +58,11 @@ def lib():
         L.kda_mla_decode_workspace_bytes.restype = i64
         L.kda_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                      i32, f, i32, vp]
+        L.kda_mla_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                             i32, i32, f, i32, vp]
         for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
                      "kda_decode_multi", "kda_mla_decode", "kda_chunk_prefill_mxfp8",
-                     "kda_conv_mxfp8"):
+                     "kda_conv_mxfp8", "kda_mla_decode_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -320,6 +324,26 @@ def kda_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, workspac
            lib().kda_mla_decode(_ptr(q), _ptr(w_uk), _ptr(w_uv), _ptr(cache), _ptr(lengths),
                                 _ptr(gate), _ptr(y), _ptr(workspace), workspace.numel(), B, H,
                                 L_max, R, Dk, Dv, scale, _dtype(q), _stream(stream)))
+
+
+def kda_mla_decode_noalloc(q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, scale=None,
+                           stream=None):
+    """kda_mla_decode with the library's static scratch instead of a workspace
+    (see kda_mla_decode_noalloc in kda.h): nothing is allocated, on the host
+    or the device."""
+    _same_dtype(q, w_uk, w_uv, cache, gate, y)
+    if lengths.dtype != torch.int32:
+        raise TypeError("lengths must be int32")
+    R, Dk, Dv = cache.shape[-1], q.shape[-1], w_uv.shape[-2]
+    if scale is None:
+        scale = Dk ** -0.5
+    _need("kda_mla_decode_noalloc", q=(q, B * H * Dk), w_uk=(w_uk, H * Dk * R),
+          w_uv=(w_uv, H * Dv * R), cache=(cache, B * L_max * R), lengths=(lengths, B),
+          gate=(gate, B * H * Dv), y=(y, B * H * Dv))
+    _check("kda_mla_decode_noalloc",
+           lib().kda_mla_decode_noalloc(_ptr(q), _ptr(w_uk), _ptr(w_uv), _ptr(cache),
+                                        _ptr(lengths), _ptr(gate), _ptr(y), B, H, L_max, R, Dk,
+                                        Dv, scale, _dtype(q), _stream(stream)))
 
 
 def kda_prefill(x, w, g, beta, gate, norm_w, H, D, cu_seqlens=None, num_seqs=1, B=1, T=None,

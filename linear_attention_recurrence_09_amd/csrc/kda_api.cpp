@@ -91,6 +91,57 @@ int check_cu(const char* fn, const int32_t* cu, int num_seqs, int64_t T, hipStre
     return KDA_OK;
 }
 
+// Argument checks shared by both latent-attention decode entry points (all
+// but the scratch).
+int mla_args(const char* fn, const void* q, const void* w_uk, const void* w_uv, const void* cache,
+             const int32_t* lengths, const void* gate, const void* y, int32_t B, int32_t H,
+             int32_t L_max, int32_t R, int32_t Dk, int32_t Dv, float scale, int32_t dtype) {
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+    if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
+    if (B > 65535) return fail(KDA_ERR_UNSUPPORTED, "%s: B must be <= 65535 (got %d)", fn, B);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (L_max < 1) return fail(KDA_ERR_INVALID_ARG, "%s: L_max must be >= 1 (got %d)", fn, L_max);
+    if (R < 1 || Dk < 1 || Dv < 1)
+        return fail(KDA_ERR_INVALID_ARG, "%s: R, Dk and Dv must be >= 1", fn);
+    if (R != 512 || Dk != 128 || Dv != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: needs R = 512, Dk = Dv = 128 (got %d, %d, %d)", fn, R,
+                    Dk, Dv);
+    if (H % 16 != 0 || H > 96)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 up to 96 (got %d)", fn, H);
+    if (!(scale > 0.f) || !(scale < 3.0e38f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    if (B == 0) return KDA_OK;
+    if (q == nullptr || w_uk == nullptr || w_uv == nullptr || cache == nullptr ||
+        lengths == nullptr || gate == nullptr || y == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: every pointer must be non-null", fn);
+    if (!aligned16(q) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
+        !aligned16(gate) || !aligned16(y))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    if ((reinterpret_cast<uintptr_t>(lengths) & 3u) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "%s: lengths must be 4-byte aligned", fn);
+    return KDA_OK;
+}
+
+// y apart from every tensor and the scratch; the scratch apart from the inputs.
+int mla_apart(const char* fn, const void* q, const void* w_uk, const void* w_uv,
+              const void* cache, const int32_t* lengths, const void* gate, const void* y,
+              const void* ws, int64_t need, int32_t B, int32_t H, int32_t L_max, int32_t R,
+              int32_t Dk, int32_t Dv) {
+    const int64_t q_b = (int64_t)B * H * Dk * 2, wk_b = (int64_t)H * Dk * R * 2;
+    const int64_t wv_b = (int64_t)H * Dv * R * 2, c_b = (int64_t)B * L_max * R * 2;
+    const int64_t g_b = (int64_t)B * H * Dv * 2, y_b = g_b, l_b = (int64_t)B * 4;
+    if (overlap(y, y_b, q, q_b) || overlap(y, y_b, w_uk, wk_b) || overlap(y, y_b, w_uv, wv_b) ||
+        overlap(y, y_b, cache, c_b) || overlap(y, y_b, lengths, l_b) || overlap(y, y_b, gate, g_b) ||
+        overlap(y, y_b, ws, need))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y must not overlap another tensor", fn);
+    if (overlap(ws, need, q, q_b) || overlap(ws, need, w_uk, wk_b) ||
+        overlap(ws, need, w_uv, wv_b) || overlap(ws, need, cache, c_b) ||
+        overlap(ws, need, lengths, l_b) || overlap(ws, need, gate, g_b))
+        return fail(KDA_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,46 +472,52 @@ int kda_mla_decode(const void* q, const void* w_uk, const void* w_uv, const void
                    int64_t workspace_bytes, int32_t B, int32_t H, int32_t L_max, int32_t R,
                    int32_t Dk, int32_t Dv, float scale, int32_t dtype, hipStream_t s) {
     const char* fn = "kda_mla_decode";
-    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
-    if (dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
-    if (B < 0) return fail(KDA_ERR_INVALID_ARG, "%s: B must be >= 0 (got %d)", fn, B);
-    if (B > 65535) return fail(KDA_ERR_UNSUPPORTED, "%s: B must be <= 65535 (got %d)", fn, B);
-    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
-    if (L_max < 1) return fail(KDA_ERR_INVALID_ARG, "%s: L_max must be >= 1 (got %d)", fn, L_max);
-    if (R < 1 || Dk < 1 || Dv < 1)
-        return fail(KDA_ERR_INVALID_ARG, "%s: R, Dk and Dv must be >= 1", fn);
-    if (R != 512 || Dk != 128 || Dv != 128)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: needs R = 512, Dk = Dv = 128 (got %d, %d, %d)", fn, R,
-                    Dk, Dv);
-    if (H % 16 != 0 || H > 96)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 up to 96 (got %d)", fn, H);
-    if (!(scale > 0.f) || !(scale < 3.0e38f))
-        return fail(KDA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    if (int rc = mla_args(fn, q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, R, Dk, Dv,
+                          scale, dtype))
+        return rc;
     if (B == 0) return ok();   // nothing to read or write
-    if (q == nullptr || w_uk == nullptr || w_uv == nullptr || cache == nullptr ||
-        lengths == nullptr || gate == nullptr || y == nullptr || workspace == nullptr)
-        return fail(KDA_ERR_INVALID_ARG, "%s: every pointer must be non-null", fn);
-    if (!aligned16(q) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(cache) ||
-        !aligned16(gate) || !aligned16(y))
-        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
-    if ((reinterpret_cast<uintptr_t>(lengths) & 3u) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "%s: lengths must be 4-byte aligned", fn);
+    if (workspace == nullptr) return fail(KDA_ERR_INVALID_ARG, "%s: workspace must be non-null", fn);
     const int64_t need = kda::mla_workspace_bytes(B, H, L_max);
     if (workspace_bytes < need)
         return fail(KDA_ERR_INVALID_ARG, "%s: workspace of %lld bytes, %lld needed", fn,
                     (long long)workspace_bytes, (long long)need);
-    const int64_t q_b = (int64_t)B * H * Dk * 2, wk_b = (int64_t)H * Dk * R * 2;
-    const int64_t wv_b = (int64_t)H * Dv * R * 2, c_b = (int64_t)B * L_max * R * 2;
-    const int64_t g_b = (int64_t)B * H * Dv * 2, y_b = g_b, l_b = (int64_t)B * 4;
-    if (overlap(y, y_b, q, q_b) || overlap(y, y_b, w_uk, wk_b) || overlap(y, y_b, w_uv, wv_b) ||
-        overlap(y, y_b, cache, c_b) || overlap(y, y_b, lengths, l_b) || overlap(y, y_b, gate, g_b) ||
-        overlap(y, y_b, workspace, need))
-        return fail(KDA_ERR_INVALID_ARG, "%s: y must not overlap another tensor", fn);
-    if (overlap(workspace, need, q, q_b) || overlap(workspace, need, w_uk, wk_b) ||
-        overlap(workspace, need, w_uv, wv_b) || overlap(workspace, need, cache, c_b) ||
-        overlap(workspace, need, lengths, l_b) || overlap(workspace, need, gate, g_b))
-        return fail(KDA_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
+    if (int rc = mla_apart(fn, q, w_uk, w_uv, cache, lengths, gate, y, workspace, need, B, H,
+                           L_max, R, Dk, Dv))
+        return rc;
     return hip_status(kda::launch_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, workspace, B,
+                                             H, L_max, scale, s),
+                      fn);
+}
+
+int kda_mla_decode_noalloc(const void* q, const void* w_uk, const void* w_uv, const void* cache,
+                           const int32_t* lengths, const void* gate, void* y, int32_t B,
+                           int32_t H, int32_t L_max, int32_t R, int32_t Dk, int32_t Dv,
+                           float scale, int32_t dtype, hipStream_t s) {
+    const char* fn = "kda_mla_decode_noalloc";
+    if (int rc = mla_args(fn, q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, R, Dk, Dv,
+                          scale, dtype))
+        return rc;
+    if (B == 0) return ok();
+    const int64_t need = kda::mla_workspace_bytes(B, H, L_max);
+    if (need > KDA_MLA_NOALLOC_MAX_BYTES)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "%s: B=%d, H=%d, L_max=%d need %lld bytes of scratch; the library's static "
+                    "scratch holds %lld (use kda_mla_decode with a workspace)",
+                    fn, B, H, L_max, (long long)need, (long long)KDA_MLA_NOALLOC_MAX_BYTES);
+    // the tensors apart from each other first (no HIP call yet), then from
+    // the scratch
+    if (int rc = mla_apart(fn, q, w_uk, w_uv, cache, lengths, gate, y, nullptr, 0, B, H, L_max,
+                           R, Dk, Dv))
+        return rc;
+    hipError_t e = hipSuccess;
+    void* scratch = kda::mla_scratch(&e);
+    if (scratch == nullptr)
+        return fail(KDA_ERR_HIP, "%s: no device address for the static scratch: %s", fn,
+                    hipGetErrorString(e));
+    if (int rc = mla_apart(fn, q, w_uk, w_uv, cache, lengths, gate, y, scratch, need, B, H,
+                           L_max, R, Dk, Dv))
+        return rc;
+    return hip_status(kda::launch_mla_decode(q, w_uk, w_uv, cache, lengths, gate, y, scratch, B,
                                              H, L_max, scale, s),
                       fn);
 }

@@ -63,6 +63,9 @@ hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, con
 // 128, H a multiple of 16 up to 96.
 int mla_splits(int B, int Lmax);
 int64_t mla_workspace_bytes(int B, int H, int Lmax);
+// The current device's address of the library's static decode scratch
+// (KDA_MLA_NOALLOC_MAX_BYTES, 256-byte aligned); null with *err set on failure.
+void* mla_scratch(hipError_t* err);
 hipError_t launch_mla_decode(const void* q, const void* w_uk, const void* w_uv,
                              const void* cache, const int32_t* lengths, const void* gate, void* y,
                              void* workspace, int B, int H, int Lmax, float scale,

@@ -21,8 +21,18 @@
 //  3. combine the splits, o = u W_uv[h]^T, y = o * sigmoid(gate).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "kda.h"
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
+
+// Device scratch of the decode entry point that allocates nothing: q' and the
+// split partials of one call, at most KDA_MLA_NOALLOC_MAX_BYTES.  Each GPU
+// that runs the library holds its own copy until the process ends.  In host
+// code this name is only a handle: the device address comes from
+// hipGetSymbolAddress (mla_scratch below).
+static __device__ __align__(256) char scratch[KDA_MLA_NOALLOC_MAX_BYTES];
 
 namespace kda {
 
@@ -422,6 +432,28 @@ int64_t mla_workspace_bytes(int B, int H, int Lmax) {
     return (int64_t)B * H * kR * 2                 // q' (bf16)
            + (int64_t)B * ns * H * 2 * 4           // m, l
            + (int64_t)B * ns * H * kR * 4 + 256;   // U, and alignment slack
+}
+
+void* mla_scratch(hipError_t* err) {
+    // looked up once per device, with that device current
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
 }
 
 hipError_t launch_mla_decode(const void* q, const void* w_uk, const void* w_uv,

@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
     assert declared() == ["kda_chunk_prefill", "kda_chunk_prefill_mxfp8", "kda_conv",
                           "kda_conv_mxfp8", "kda_decode_multi", "kda_decode_step",
                           "kda_gated_norm", "kda_last_error", "kda_mla_decode",
-                          "kda_mla_decode_workspace_bytes", "kda_version"]
+                          "kda_mla_decode_noalloc", "kda_mla_decode_workspace_bytes",
+                          "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -221,3 +222,32 @@ def test_mla_decode_argument_checks(L):
     assert "kda_mla_decode" in kda.kda_last_error()
     assert mla(B=0, wsb=0) == OK
     assert mla(B=0, wsb=0, q=None, ws=None) == OK            # an empty batch reads no pointer
+
+
+def test_mla_decode_noalloc_argument_checks(L):
+    """The allocation-free decode refuses, on the host and before any HIP
+    call, what kda_mla_decode refuses, and any request whose workspace would
+    exceed its static scratch."""
+    B, H, Lm = 2, 96, 64
+    cap = 128 << 20
+    assert kda.KDA_MLA_NOALLOC_MAX_BYTES == cap
+    assert "(128LL << 20)" in open(HEADER).read()
+
+    def na(q=A, wk=A + 32 * MB, wv=A + 64 * MB, c=A + 96 * MB, ln=A + 100 * MB, g=A + 102 * MB,
+           y=A + 104 * MB, B=B, H=H, Lm=Lm, R=512, Dk=128, Dv=128, scale=0.088, dt=1):
+        return L.kda_mla_decode_noalloc(q, wk, wv, c, ln, g, y, B, H, Lm, R, Dk, Dv,
+                                        ctypes.c_float(scale), dt, None)
+    assert na(q=None) == INVALID
+    assert na(dt=0) == UNSUPPORTED
+    assert na(H=112) == UNSUPPORTED
+    assert na(R=256) == UNSUPPORTED
+    assert na(Lm=0) == INVALID
+    assert na(scale=0.0) == INVALID
+    assert na(y=A + 16) == INVALID                           # y overlaps q
+    assert na(c=A + 96 * MB + 8) == INVALID                  # misaligned cache
+    assert na(B=0) == OK and na(B=0, q=None) == OK           # an empty batch reads nothing
+    # the decode workload (256 x 96 heads) fits; 4096 sequences do not
+    assert L.kda_mla_decode_workspace_bytes(256, 96, 4096) <= cap
+    assert L.kda_mla_decode_workspace_bytes(4096, 96, 64) > cap
+    assert na(B=4096, Lm=64) == INVALID
+    assert "static scratch" in kda.kda_last_error()
