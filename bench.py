@@ -314,6 +314,47 @@ def parity_figures(gpu, ref, block=16):
             "max_abs": ma, "max_abs_over_rms": ma / rms}
 
 
+def bench_fused_prefill(kda, torch, stream, x, w, g, beta, gate, nw, H, D, steps, warmup):
+    """kda_prefill_fused on the same inputs as the three-call step: the conv,
+    SiLU and L2 inside the recurrence kernel, then the gated norm (y written
+    over o).  HIP events on the launch stream; the fused floor is the bytes a
+    single pass would move (x, g, beta, gate in, y out), this path's bytes
+    add the recurrence's o out and back in."""
+    N = x.shape[0]
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        kda.kda_prefill_fused(x, w, g, beta, gate, nw, o, o, H, D, B=1, T=N, final_state=sT,
+                              stream=stream)
+
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms = sum(per) / steps
+    P = 3 * H * D
+    floor_b = N * P * 2 + 2 * N * H * D * 2 + N * H * 2 + N * H * D * 2      # x, g, gate, beta, y
+    path_b = floor_b + 2 * N * H * D * 2                                     # + o out and in
+    log(f"fused prefill: {ms:.3f} ms/step ({N / ms / 1e3:.2f} M tokens/s)")
+    del o, sT
+    return {"workload": f"prefill_T{N}_H{H}_D{D}_bf16 through kda_prefill_fused (conv + SiLU + L2 "
+                        f"inside the recurrence kernel, then the gated norm)",
+            "tokens": N, "steps": steps, "ms_per_step": ms,
+            "ms_median_min_max": [per[len(per) // 2], per[0], per[-1]],
+            "tokens_per_s": N / (ms * 1e-3),
+            "fused_floor_bytes": floor_b, "fused_floor_ms": floor_b / HBM_PEAK_GBS / 1e6,
+            "path_bytes": path_b, "path_floor_ms": path_b / HBM_PEAK_GBS / 1e6,
+            "hbm_frac_of_fused_floor": floor_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(inp, spec, T_s, H_s, gpu_out):
     """The CPU oracle on the first T_s tokens of the first H_s heads (all its
     threads), plus one-thread figures on the tiny workload and on a sample of
@@ -532,6 +573,9 @@ def main():
         "kernels_ms": k_ms,
         "pipeline_gbs": sum(nbytes.values()) / (ms_step * 1e-3) / 1e9,
     }
+
+    result["prefill_T65536_fused"] = bench_fused_prefill(
+        kda, torch, stream, x, w, g, beta, gate, nw, H, D, args.steps, args.warmup)
 
     result["prefill_T65536_mxfp8"] = bench_mxfp8_prefill(
         kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D, args.steps, args.warmup)

@@ -188,6 +188,42 @@ int kda_chunk_prefill_mxfp8(const void* q, const void* q_scale, const void* k,
                             hipStream_t s);
 
 /*
+ * kda_prefill_fused -- the whole prefill path with the short conv run inside
+ * the chunked recurrence: the recurrence's producer waves read the projected
+ * inputs before the conv and compute the conv, SiLU and the L2 norm of q and
+ * k themselves, so q, k and v never go through memory; then the gated head
+ * RMSNorm.  ("Inside Kimi K3", KDA short-convolution diagram and KDA one-head
+ * diagram: projections -> conv + SiLU -> L2 norm of q, k -> recurrent state
+ * -> head RMSNorm times a sigmoid gate.)  Same results as kda_conv ->
+ * kda_chunk_prefill (16-token chunks) -> kda_gated_norm up to rounding: q
+ * and k are normalised in fp32 here instead of passing through bf16 first.
+ *
+ *   x, conv_w, conv_state_in, conv_state_out, cu_seqlens, num_seqs, B, T, H,
+ *   D, l2_eps          as in kda_conv
+ *   g, beta, initial_state, final_state
+ *                      as in kda_chunk_prefill (DK = DV = D)
+ *   gate, norm_w, rms_eps
+ *                      as kda_gated_norm's gate, weight and eps
+ *   o                  [B*T, H, D] the recurrence's output S_t^T q_t (the
+ *                      norm's input); may equal y
+ *   y                  [B*T, H, D] the gated RMSNorm of o
+ * Launches the fused recurrence kernel, the rolling-state pass (when
+ * conv_state_out is given) and the gated norm, in that order on `s`.  The
+ * gated norm is a separate pass: a head's 128 value columns are split over
+ * two workgroups, and the norm needs all of them.  bf16 only (fp32 returns
+ * KDA_ERR_UNSUPPORTED); D = 64 or 128.  final_state may equal initial_state
+ * and conv_state_out may equal conv_state_in (updated in place); o and y
+ * overlap no input and nothing else.
+ */
+int kda_prefill_fused(const void* x, const float* conv_w, const void* g, const void* beta,
+                      const void* gate, const float* norm_w, void* o, void* y,
+                      const void* conv_state_in, void* conv_state_out,
+                      const float* initial_state, float* final_state,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                      int32_t H, int32_t D, int32_t dtype, float l2_eps, float rms_eps,
+                      hipStream_t s);
+
+/*
  * kda_decode_step -- one new token for each of B sequences: the conv window
  * [conv_state (3 values), x_t] per channel, SiLU, L2 of q and k, then one
  * gated-delta-rule step.  ("Inside Kimi K3", KDA short-convolution diagram,

@@ -13,6 +13,7 @@ import torch
 
 __all__ = ["KdaError", "lib", "kda_version", "kda_last_error", "kda_conv", "kda_chunk_prefill",
            "kda_decode_step", "kda_decode_multi", "kda_gated_norm", "kda_prefill",
+           "kda_prefill_fused",
            "kda_mla_decode_workspace_bytes", "kda_mla_decode", "kda_mla_decode_noalloc",
            "kda_chunk_prefill_mxfp8", "kda_conv_mxfp8", "KDA_MLA_NOALLOC_MAX_BYTES",
            "KDA_F32",
@@ -60,9 +61,11 @@ def lib():
                                      i32, f, i32, vp]
         L.kda_mla_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                              i32, i32, f, i32, vp]
+        L.kda_prefill_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                        i32, i32, i32, i32, i32, f, f, vp]
         for name in ("kda_conv", "kda_chunk_prefill", "kda_decode_step", "kda_gated_norm",
                      "kda_decode_multi", "kda_mla_decode", "kda_chunk_prefill_mxfp8",
-                     "kda_conv_mxfp8", "kda_mla_decode_noalloc"):
+                     "kda_conv_mxfp8", "kda_mla_decode_noalloc", "kda_prefill_fused"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -344,6 +347,34 @@ def kda_mla_decode_noalloc(q, w_uk, w_uv, cache, lengths, gate, y, B, H, L_max, 
            lib().kda_mla_decode_noalloc(_ptr(q), _ptr(w_uk), _ptr(w_uv), _ptr(cache),
                                         _ptr(lengths), _ptr(gate), _ptr(y), B, H, L_max, R, Dk,
                                         Dv, scale, _dtype(q), _stream(stream)))
+
+
+def kda_prefill_fused(x, w, g, beta, gate, norm_w, o, y, H, D, cu_seqlens=None, num_seqs=1,
+                      B=1, T=None, conv_state_in=None, conv_state_out=None, initial_state=None,
+                      final_state=None, l2_eps=1e-6, rms_eps=1e-6, stream=None):
+    """The prefill path with the conv run inside the recurrence kernel (see
+    kda_prefill_fused in kda.h): bf16 x [N, 3HD], g, gate, o, y [N, H, D],
+    beta [N, H]; o may be y."""
+    N = x.shape[0]
+    if T is None:
+        T = N if cu_seqlens is not None else N // B
+    _same_dtype(x, g, beta, gate, o, y, conv_state_in, conv_state_out)
+    _f32(w, norm_w, initial_state, final_state)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    ns, Nt = _tokens(B, T, cu_seqlens, num_seqs)
+    P = 3 * H * D
+    _need("kda_prefill_fused", x=(x, Nt * P), w=(w, P * 4), g=(g, Nt * H * D),
+          beta=(beta, Nt * H), gate=(gate, Nt * H * D), norm_w=(norm_w, D), o=(o, Nt * H * D),
+          y=(y, Nt * H * D), conv_state_in=(conv_state_in, ns * P * 3),
+          conv_state_out=(conv_state_out, ns * P * 3),
+          initial_state=(initial_state, ns * H * D * D), final_state=(final_state, ns * H * D * D))
+    _check("kda_prefill_fused",
+           lib().kda_prefill_fused(_ptr(x), _ptr(w), _ptr(g), _ptr(beta), _ptr(gate),
+                                   _ptr(norm_w), _ptr(o), _ptr(y), _ptr(conv_state_in),
+                                   _ptr(conv_state_out), _ptr(initial_state), _ptr(final_state),
+                                   _ptr(cu_seqlens), num_seqs if cu_seqlens is not None else 0,
+                                   B, T, H, D, _dtype(x), l2_eps, rms_eps, _stream(stream)))
 
 
 def kda_prefill(x, w, g, beta, gate, norm_w, H, D, cu_seqlens=None, num_seqs=1, B=1, T=None,

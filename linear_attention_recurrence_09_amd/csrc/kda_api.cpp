@@ -340,6 +340,81 @@ int kda_chunk_prefill_mxfp8(const void* q, const void* q_scale, const void* k,
                       fn);
 }
 
+int kda_prefill_fused(const void* x, const float* conv_w, const void* g, const void* beta,
+                      const void* gate, const float* norm_w, void* o, void* y,
+                      const void* conv_state_in, void* conv_state_out,
+                      const float* initial_state, float* final_state,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                      int32_t H, int32_t D, int32_t dtype, float l2_eps, float rms_eps,
+                      hipStream_t s) {
+    const char* fn = "kda_prefill_fused";
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+    if (dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: bf16 only (fp32 runs kda_conv, kda_chunk_prefill and "
+                    "kda_gated_norm)", fn);
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "%s: H must be >= 1 (got %d)", fn, H);
+    if (!valid_head(D)) return fail(KDA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, D);
+    if (!(l2_eps > 0.f) || !(rms_eps > 0.f))
+        return fail(KDA_ERR_INVALID_ARG, "%s: l2_eps and rms_eps must be > 0", fn);
+    if (x == nullptr || conv_w == nullptr || g == nullptr || beta == nullptr || gate == nullptr ||
+        norm_w == nullptr || o == nullptr || y == nullptr)
+        return fail(KDA_ERR_INVALID_ARG, "%s: x, conv_w, g, beta, gate, norm_w, o and y must be "
+                    "non-null", fn);
+    int ns;
+    int64_t N;
+    if (int rc = seq_layout(fn, cu_seqlens, num_seqs, B, T, &ns, &N)) return rc;
+    if (int rc = check_cu(fn, cu_seqlens, ns, N, s)) return rc;
+    if ((int64_t)ns * H * (D / 64) > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "%s: too many (sequence, head) pairs", fn);
+    if (!aligned16(x) || !aligned16(g) || !aligned16(beta) || !aligned16(gate) ||
+        !aligned16(norm_w) || !aligned16(o) || !aligned16(y) || !aligned16(conv_state_in) ||
+        !aligned16(conv_state_out) || !aligned16(initial_state) || !aligned16(final_state))
+        return fail(KDA_ERR_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+    const int64_t P = 3LL * H * D;
+    const int64_t x_b = N * P * 2, t_b = N * H * D * 2, b_b = N * H * 2;
+    const int64_t cs_b = (int64_t)ns * P * 3 * 2, st_b = (int64_t)ns * H * D * D * 4;
+    const void* ins[6] = {x, g, beta, gate, conv_state_in, initial_state};
+    const int64_t in_b[6] = {x_b, t_b, b_b, t_b, cs_b, st_b};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(o, t_b, ins[i], in_b[i]))
+            return fail(KDA_ERR_INVALID_ARG, "%s: o must not overlap an input", fn);
+        if (overlap(y, t_b, ins[i], in_b[i]))
+            return fail(KDA_ERR_INVALID_ARG, "%s: y must not overlap an input", fn);
+    }
+    if (y != o && overlap(y, t_b, o, t_b))
+        return fail(KDA_ERR_INVALID_ARG, "%s: y partially overlaps o", fn);
+    if (final_state != nullptr) {
+        if ((const void*)final_state != (const void*)initial_state &&
+            overlap(final_state, st_b, initial_state, st_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: final_state partially overlaps initial_state", fn);
+        for (int i = 0; i < 5; ++i)
+            if (overlap(final_state, st_b, ins[i], in_b[i]) || overlap(final_state, st_b, o, t_b) ||
+                overlap(final_state, st_b, y, t_b))
+                return fail(KDA_ERR_INVALID_ARG, "%s: final_state overlaps another tensor", fn);
+    }
+    if (conv_state_out != nullptr) {
+        if (conv_state_out != conv_state_in && overlap(conv_state_out, cs_b, conv_state_in, cs_b))
+            return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out partially overlaps conv_state_in",
+                        fn);
+        for (int i = 0; i < 4; ++i)
+            if (overlap(conv_state_out, cs_b, ins[i], in_b[i]) ||
+                overlap(conv_state_out, cs_b, o, t_b) || overlap(conv_state_out, cs_b, y, t_b) ||
+                overlap(conv_state_out, cs_b, initial_state, st_b) ||
+                overlap(conv_state_out, cs_b, final_state, st_b))
+                return fail(KDA_ERR_INVALID_ARG, "%s: conv_state_out overlaps another tensor", fn);
+    }
+    if (ns == 0) return ok();
+    hipError_t e = kda::launch_chunk_pipe_conv(x, conv_w, conv_state_in, g, beta, o,
+                                               initial_state, final_state, cu_seqlens, ns, T, H,
+                                               D, l2_eps, s);
+    if (e == hipSuccess)
+        e = kda::launch_conv_state(x, conv_state_in, conv_state_out, cu_seqlens, ns, T, N, H, D,
+                                   dtype, s);
+    if (e == hipSuccess && N > 0)
+        e = kda::launch_gated_norm(o, gate, norm_w, y, N * H, D, rms_eps, dtype, s);
+    return hip_status(e, fn);
+}
+
 int kda_decode_step(const void* x, const float* w, void* conv_state, const void* g,
                     const void* beta, float* state, void* o, int32_t B, int32_t H, int32_t D,
                     int32_t dtype, float l2_eps, hipStream_t s) {

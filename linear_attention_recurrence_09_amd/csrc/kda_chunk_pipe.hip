@@ -50,6 +50,8 @@
 // values; V codes are decoded the same way and stored to the slot as bf16
 // (exact).  Everything after that is the bf16 kernel's code, so on the
 // decoded values both give bitwise equal results.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -65,6 +67,7 @@ typedef __attribute__((address_space(3))) bf16v4* lds_bf16v4_ptr;
 constexpr int kNP = 8;                 // producer waves (two per SIMD)
 constexpr int kRing = 8;               // LDS slots
 constexpr int kSpinLimit = 1 << 17;    // polls (about 128 cycles each) before giving up
+constexpr int kOob = 0x40000000;       // a buffer offset past every range here (reads give 0)
 constexpr int kSleep = 2;              // s_sleep argument between polls (64 cycles each)
 
 template <int DK, int DVS>
@@ -253,11 +256,16 @@ __device__ __forceinline__ bool wait_at_least(int* f, int target, int* stop) {
     return true;
 }
 
-// Element type of q, k, v and g: bf16, or MXFP8 (E4M3 codes, with one E8M0
-// scale byte per 32 consecutive channels in separate [tokens, H, D/32]
-// tensors).
-template <bool MX> struct PipeIn { using type = __bf16; };
-template <> struct PipeIn<true> { using type = uint8_t; };
+// What the producers read for q, k and v:
+//  kInBf16  q, k (L2-normalised) and v in bf16, e.g. kda_conv's output;
+//  kInMx    the same as MXFP8 (E4M3 codes with one E8M0 scale byte per 32
+//           consecutive channels in separate [tokens, H, D/32] tensors);
+//  kInConv  the projected inputs before the short convolution: the producers
+//           run the conv, SiLU and (for q, k) the L2 norm themselves.
+// g is bf16 (kInBf16, kInConv) or MXFP8 (kInMx).
+constexpr int kInBf16 = 0, kInMx = 1, kInConv = 2;
+template <int IN> struct PipeIn { using type = __bf16; };
+template <> struct PipeIn<kInMx> { using type = uint8_t; };
 
 // lane n of the lane's 16-lane row, for a token index known after unrolling
 __device__ __forceinline__ float row_bcast_t(float x, int t) {
@@ -279,24 +287,32 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
     return __builtin_bit_cast(float, bits);
 }
 
-template <int DK, int DVS, bool MX = false, int THREADS = PipeCfg<DK, DVS>::THREADS>
+template <int DK, int DVS, int IN = kInBf16, int THREADS = PipeCfg<DK, DVS>::THREADS>
 __global__ void __launch_bounds__(THREADS)
-chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
-                  const typename PipeIn<MX>::type* __restrict__ k,
-                  const typename PipeIn<MX>::type* __restrict__ v, int64_t stride,
-                  const typename PipeIn<MX>::type* __restrict__ g,
+chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
+                  const typename PipeIn<IN>::type* __restrict__ k,
+                  const typename PipeIn<IN>::type* __restrict__ v, int64_t stride,
+                  const typename PipeIn<IN>::type* __restrict__ g,
                   const __bf16* __restrict__ beta, __bf16* __restrict__ o, const float* s0,
                   float* sT, const int32_t* __restrict__ cu, int num_seqs, int T_len, int H,
                   int DV, int nsplit, const uint8_t* __restrict__ qsc,
                   const uint8_t* __restrict__ ksc, const uint8_t* __restrict__ vsc,
-                  const uint8_t* __restrict__ gsc) {
+                  const uint8_t* __restrict__ gsc, const float* __restrict__ cw,
+                  const __bf16* __restrict__ cs_in, float l2_eps, int blocked) {
+    constexpr bool MX = IN == kInMx, CV = IN == kInConv;
     static_assert(!MX || DK == 128, "MXFP8 inputs: two channels per producer lane");
+    static_assert(!CV || DVS == 64, "conv inputs: a value slice of 64 columns");
     constexpr int ES = MX ? 1 : 2;   // bytes per q, k, v, g element
     using Cfg = PipeCfg<DK, DVS>;
     constexpr int NC = Cfg::NC, NKS = Cfg::NKS, NKT = Cfg::NKT;
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
+    // conv inputs: the workgroup's conv taps (q and k channels of the head,
+    // then its value columns), 4 floats each, behind the ring
+    constexpr int O_W = Cfg::BYTES;
+    constexpr int WBYTES = CV ? (2 * DK + DVS) * 16 : 0;
+    static_assert(Cfg::BYTES + WBYTES <= 160 * 1024 - 256, "LDS budget (conv taps)");
 
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES + WBYTES];
     // ready[kRing], released[kRing][NC] (one counter per consumer), stop
     constexpr int NFLAGS = kRing + kRing * NC + 1;
     __shared__ __attribute__((aligned(16))) int flags[NFLAGS];
@@ -311,28 +327,39 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int lq = lane >> 4;
 
     // ---- workgroup -> (sequence, head, value slice).  Workgroups are dealt to
-    // the 8 XCDs in turn (ids x, x+8, ... run on XCD x), so XCD x is given a
-    // contiguous run of chains: the value slices of a chain sit 8 ids apart
-    // on one XCD, and a token's beta and block-scale bytes for that XCD's
-    // heads are one short contiguous range of its row, fetched into its L2
-    // once instead of every XCD fetching the whole row ---------------------
+    // the 8 XCDs in turn (ids x, x+8, ... run on XCD x), and the value slices
+    // of a chain sit 8 ids apart, on one XCD.  With blocked heads (and heads
+    // that split evenly) XCD x takes heads [x H/8, (x+1) H/8) of every
+    // sequence, the sequences in order, so a token's block-scale and beta
+    // bytes for an XCD's heads are one short run of its row, fetched into that
+    // XCD's L2 alone (chosen for MXFP8 inputs and for several sequences, where
+    // it measured faster); otherwise consecutive chains go to consecutive
+    // XCDs (faster for one sequence of bf16 inputs) -------------------------
     const int nchain = num_seqs * H;
     const int total = nchain * nsplit;
     const int bid = blockIdx.x;
-    const int span = 8 * nsplit;
-    const int full = (total / span) * span;
-    int chain, split;
-    if (bid < full) {
-        const int j = bid >> 3, xcd = bid & 7;
-        chain = xcd * (full / span) + j / nsplit;
+    int seq, head, split;
+    if (blocked && H % 8 == 0) {
+        const int hpx = H / 8, j = bid >> 3, idx = j / nsplit;
         split = j % nsplit;
+        seq = idx / hpx;
+        head = (bid & 7) * hpx + idx % hpx;
     } else {
-        const int r = bid - full;
-        chain = full / nsplit + r / nsplit;
-        split = r % nsplit;
+        const int span = 8 * nsplit;
+        const int full = (total / span) * span;
+        int chain;
+        if (bid < full) {
+            const int gi = bid >> 3;
+            chain = (gi / nsplit) * 8 + (bid & 7);
+            split = gi % nsplit;
+        } else {
+            const int r = bid - full;
+            chain = full / nsplit + r / nsplit;
+            split = r % nsplit;
+        }
+        seq = chain / H;
+        head = chain % H;
     }
-    const int seq = chain / H;
-    const int head = chain % H;
     const int n0 = split * DVS;
     // packed offsets are clamped to the T_len tokens of the batch, so offsets
     // that are not monotone or exceed it never move an access out of bounds
@@ -346,6 +373,20 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     const int nch = (int)n_chunks;
 
     if (tid < NFLAGS) flags[tid] = 0;
+    if constexpr (CV) {
+        // conv taps of this workgroup: the head's DK q channels, its DK k
+        // channels, then its DVS value columns (the k and v parts of the
+        // filter banks start H*DK and 2*H*DK channels in)
+        float* wl = reinterpret_cast<float*>(smem + O_W);
+        for (int i = tid; i < (2 * DK + DVS) * 4; i += THREADS) {
+            const int r = i >> 2;
+            const int64_t ch = r < DK ? (int64_t)head * DK + r
+                                      : (r < 2 * DK ? (int64_t)H * DK + head * DK + (r - DK)
+                                                    : 2LL * H * DK + (int64_t)head * DV + n0 +
+                                                          (r - 2 * DK));
+            wl[i] = cw[ch * 4 + (i & 3)];
+        }
+    }
     __syncthreads();
 
     if (wave >= NC) {
@@ -364,6 +405,14 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         // (block b, token t) holding (t, b) -- row b of lanes serves block b
         u32x4 rvm;
         uint32_t rvs, rsg, rsk, rsq;
+        // conv inputs: the raw x words of the lane's q and k channels for the
+        // chunk's tokens t0-3 .. t0+15 (row j = token t0-3+j), the conv state
+        // words of those channels (first chunk of a sequence only), and for V
+        // the raw x words of columns n0+2cp, +1 (cp = lane % 32) for the tokens
+        // t0+8h-3 .. t0+8h+7 (h = lane / 32) with their state words
+        uint32_t rxq[CV ? 19 : 1], rxk[CV ? 19 : 1], rcq[3], rck[3];
+        uint32_t rxv[CV ? 11 : 1], rsv[3];
+        const int cp = lane & 31, hv = lane >> 5;
         // beta of token lr as a zero-extended 32-bit word (16-bit values would
         // be packed in pairs right after the loads, which makes the wave wait)
         uint32_t rbl;
@@ -384,17 +433,54 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             const int64_t rem = t_end - t0;
             return (int)(rem < 16 ? (rem > 0 ? rem : 0) : 16);
         };
+        // conv inputs: the chunk's rows come through one resource, the 3 rows
+        // before it through another, which is empty on a sequence's first
+        // chunk (whose halo is the conv state, through a resource that is
+        // empty on every other chunk); the per-lane offsets do not depend on
+        // the chunk
+        auto halo_rsrc = [&](const __bf16* base, int64_t ci, int64_t t0, int valid) -> rsrc_t {
+            const bool on = ci > 0 && valid > 0;
+            return make_rsrc(base + (on ? t0 - 3 : t0) * stride, on ? (uint32_t)(3 * kv_row) : 0u);
+        };
         auto issue_gkq = [&](int64_t ci) {
             int64_t t0;
             const int valid = chunk_rows(ci, t0);
             const rsrc_t r_g = make_rsrc(g + (t0 * H + head) * DK, (uint32_t)(valid * g_row));
-            const rsrc_t r_k = make_rsrc(k + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
-            const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
+            if constexpr (CV) {
+                const __bf16* bq = q + (int64_t)head * DK;
+                const __bf16* bk = k + (int64_t)head * DK;
+                const rsrc_t r_q = make_rsrc(bq + t0 * stride, (uint32_t)(valid * kv_row));
+                const rsrc_t r_k = make_rsrc(bk + t0 * stride, (uint32_t)(valid * kv_row));
+                const rsrc_t h_q = halo_rsrc(bq, ci, t0, valid);
+                const rsrc_t h_k = halo_rsrc(bk, ci, t0, valid);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                rg[t] = load_word(r_g, t * g_row + c0 * ES);
-                rk[t] = load_word(r_k, t * kv_row + c0 * ES);
-                rq[t] = load_word(r_q, t * kv_row + c0 * ES);
+                for (int j = 0; j < 19; ++j) {
+                    rxq[j] = load_word(j < 3 ? h_q : r_q, (j < 3 ? j : j - 3) * kv_row + c0 * 2);
+                    rxk[j] = load_word(j < 3 ? h_k : r_k, (j < 3 ? j : j - 3) * kv_row + c0 * 2);
+                }
+                const bool st = ci == 0 && cs_in != nullptr;
+                const int64_t sb = ((int64_t)seq * stride + (int64_t)head * DK) * 3;
+                const uint32_t sbytes = st ? (uint32_t)(DK * 3 * 2) : 0u;
+                const rsrc_t s_q = make_rsrc(st ? cs_in + sb : q, sbytes);
+                const rsrc_t s_k = make_rsrc(st ? cs_in + sb + (int64_t)H * DK * 3 : q, sbytes);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    rcq[j] = load_word(s_q, c0 * 6 + j * 2 * CPL);
+                    rck[j] = load_word(s_k, c0 * 6 + j * 2 * CPL);
+                }
+            }
+            if constexpr (CV) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) rg[t] = load_word(r_g, t * g_row + c0 * ES);
+            } else {
+                const rsrc_t r_k = make_rsrc(k + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
+                const rsrc_t r_q = make_rsrc(q + t0 * stride + (int64_t)head * DK, (uint32_t)(valid * kv_row));
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    rg[t] = load_word(r_g, t * g_row + c0 * ES);
+                    rk[t] = load_word(r_k, t * kv_row + c0 * ES);
+                    rq[t] = load_word(r_q, t * kv_row + c0 * ES);
+                }
             }
             if constexpr (MX) {
                 const int64_t sb = (t0 * H + head) * (DK / 32);
@@ -410,6 +496,30 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
         auto issue_v = [&](int64_t ci) {
             int64_t t0;
             const int valid = chunk_rows(ci, t0);
+            if constexpr (CV) {
+                // row r of this lane is token t0 + 8 hv - 3 + r: rows before t0
+                // (first half, r < 3) come from the halo resource and get an
+                // out-of-range offset (kOob, past any range) in the main one,
+                // and the other way round
+                const __bf16* bv = v + (int64_t)head * DV + n0;
+                const rsrc_t r_v = make_rsrc(bv + t0 * stride, (uint32_t)(valid * kv_row));
+                const rsrc_t h_v = halo_rsrc(bv, ci, t0, valid);
+#pragma unroll
+                for (int r = 0; r < 11; ++r) {
+                    const int off = r < 3 && hv == 0 ? kOob : (8 * hv - 3 + r) * kv_row + cp * 4;
+                    rxv[r] = __builtin_amdgcn_raw_buffer_load_b32(r_v, off, 0, 0);
+                    if (r < 3)
+                        rxv[r] |= __builtin_amdgcn_raw_buffer_load_b32(h_v, hv ? kOob : r * kv_row + cp * 4, 0, 0);
+                }
+                // the state of columns n0+2cp, +1 (lanes of the first half only)
+                const bool st = ci == 0 && cs_in != nullptr;
+                const int64_t sb = ((int64_t)seq * stride + 2LL * H * DK + (int64_t)head * DV + n0) * 3;
+                const rsrc_t s_v = make_rsrc(st ? cs_in + sb : v, st ? (uint32_t)(DVS * 3 * 2) : 0u);
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    rsv[j] = __builtin_amdgcn_raw_buffer_load_b32(s_v, hv ? kOob : cp * 12 + 4 * j, 0, 0);
+                return;
+            }
             const rsrc_t r_v = make_rsrc(v + t0 * stride + (int64_t)head * DV + n0, (uint32_t)(valid * kv_row));
             if constexpr (MX) {
                 rvm = __builtin_amdgcn_raw_buffer_load_b128(r_v, vt * kv_row + vc, 0, 0);
@@ -451,6 +561,111 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
             const bool go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+            char* slot = smem + s * SLOT;
+
+            // ---- conv inputs: short conv, SiLU, L2 of q and k ------------------
+            // ("Inside Kimi K3", KDA short-convolution diagram: 4 taps per
+            // channel over x_{t-3} .. x_t, then SiLU; KDA one-head diagram: L2
+            // norm of q and k.)  V goes to the slot in bf16; q and k stay in
+            // rq / rk as bf16 words before the norm, and inv_l holds the
+            // inverse norm of (token, part) = (l/2 % 16, l/32) for lane l
+            float inv_l = 1.f;
+            if constexpr (CV) {
+                const float* wl = reinterpret_cast<const float*>(smem + O_W);
+                // on the first chunk the 3 rows before it come from the state
+                // words: per channel pair the three words hold
+                // [s0 c | s1 c], [s2 c | s0 c'], [s1 c' | s2 c'] (CPL = 2)
+                auto halo = [](uint32_t (&x)[3], const uint32_t (&st)[3]) {
+                    if constexpr (CPL == 2) {
+                        x[0] |= __builtin_amdgcn_perm(st[1], st[0], 0x07060100u);
+                        x[1] |= __builtin_amdgcn_perm(st[2], st[0], 0x05040302u);
+                        x[2] |= __builtin_amdgcn_perm(st[2], st[1], 0x07060100u);
+                    } else {
+                        x[0] |= st[0];
+                        x[1] |= st[1];
+                        x[2] |= st[2];
+                    }
+                };
+                // V: columns n0 + 2cp, +1 of tokens 8hv .. 8hv + 7
+                {
+                    uint32_t hx[3] = {rxv[0], rxv[1], rxv[2]};
+                    uint32_t hs[3] = {rsv[0], rsv[1], rsv[2]};
+                    // (a column pair's state: [s0 c | s1 c], [s2 c | s0 c'], [s1 c' | s2 c'])
+                    hx[0] |= __builtin_amdgcn_perm(hs[1], hs[0], 0x07060100u);
+                    hx[1] |= __builtin_amdgcn_perm(hs[2], hs[0], 0x05040302u);
+                    hx[2] |= __builtin_amdgcn_perm(hs[2], hs[1], 0x07060100u);
+                    const floatx4 w[2] = {*reinterpret_cast<const floatx4*>(wl + (2 * DK + 2 * cp) * 4),
+                                          *reinterpret_cast<const floatx4*>(wl + (2 * DK + 2 * cp + 1) * 4)};
+                    auto xv = [&](int r, int j) { return chan(r < 3 ? hx[r] : rxv[r], j); };
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        float y[2];
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            y[j] = siluf_(w[j][0] * xv(t, j) + w[j][1] * xv(t + 1, j) +
+                                          w[j][2] * xv(t + 2, j) + w[j][3] * xv(t + 3, j));
+                        *reinterpret_cast<uint32_t*>(slot + Cfg::O_V + (8 * hv + t) * Cfg::PV + cp * 4) =
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{y[0], y[1]}, bf16x2));
+                    }
+                }
+                // q and k: conv + SiLU per channel, squares summed per token
+                float ss[32];   // [part][token]
+                auto conv_part = [&](const uint32_t (&rx)[19], const uint32_t (&rs)[3], int part,
+                                     uint32_t (&out)[16]) {
+                    uint32_t hx[3] = {rx[0], rx[1], rx[2]};
+                    halo(hx, rs);
+                    floatx4 w[CPL];
+#pragma unroll
+                    for (int j = 0; j < CPL; ++j) w[j] = *reinterpret_cast<const floatx4*>(wl + (part * DK + c0 + j) * 4);
+                    auto xv = [&](int r, int j) { return chan(r < 3 ? hx[r] : rx[r], j); };
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) {
+                        float sq = 0.f, y[CPL];
+#pragma unroll
+                        for (int j = 0; j < CPL; ++j) {
+                            y[j] = siluf_(w[j][0] * xv(t, j) + w[j][1] * xv(t + 1, j) +
+                                          w[j][2] * xv(t + 2, j) + w[j][3] * xv(t + 3, j));
+                            sq += y[j] * y[j];
+                        }
+                        ss[16 * part + t] = sq;
+                        out[t] = pack(y);
+                    }
+                };
+                conv_part(rxq, rcq, 0, rq);
+                conv_part(rxk, rck, 1, rk);
+                // sums over the 64 lanes: at each step a lane keeps half of
+                // its values (the upper half when its lane bit is set) and adds
+                // the partner's copy of them; lane l ends with value l/2
+                auto step = [&](auto n_c, int m, auto xchg) {
+                    constexpr int n = decltype(n_c)::value;
+                    const bool up = (lane & m) != 0;
+#pragma unroll
+                    for (int i = 0; i < n / 2; ++i) {
+                        const float send = up ? ss[i] : ss[i + n / 2];
+                        const float keep = up ? ss[i + n / 2] : ss[i];
+                        ss[i] = keep + xchg(send);
+                    }
+                };
+                auto bperm = [&](float x, int m) {
+                    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), __builtin_bit_cast(int, x)));
+                };
+                auto dpp = [](float x, auto ctrl_c) {
+                    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                                              decltype(ctrl_c)::value, 0xF, 0xF, true));
+                };
+                using I32 = std::integral_constant<int, 32>;
+                using I16 = std::integral_constant<int, 16>;
+                using I8 = std::integral_constant<int, 8>;
+                using I4 = std::integral_constant<int, 4>;
+                using I2 = std::integral_constant<int, 2>;
+                step(I32{}, 32, [&](float x) { return bperm(x, 32); });
+                step(I16{}, 16, [&](float x) { return bperm(x, 16); });
+                step(I8{}, 8, [&](float x) { return dpp(x, std::integral_constant<int, 0x128>{}); });   // row_ror:8
+                step(I4{}, 4, [&](float x) { return dpp(x, std::integral_constant<int, 0x141>{}); });   // row_half_mirror
+                step(I2{}, 2, [&](float x) { return dpp(x, std::integral_constant<int, 0x4E>{}); });    // quad_perm 2,3,0,1
+                const float tot = ss[0] + dpp(ss[0], std::integral_constant<int, 0xB1>{});            // quad_perm 1,0,3,2
+                inv_l = rsqrt_nr(tot + l2_eps);
+            }
 
             // ---- decay products, in registers -------------------------------
             // a_t = e^{g_t}; F_t = e^{G_t} = a_0 .. a_t (forward), then
@@ -470,18 +685,34 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
                 if constexpr (MX) return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, row_bcast_t(fs, t), false)[j];
                 else return chan(w, j);
             };
+            // conv inputs: q and k of token t times their inverse norms
+            auto inv_q = [&](int t) -> float {
+                if constexpr (CV) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_l), 2 * t));
+                else return 1.f;
+            };
+            auto inv_k = [&](int t) -> float {
+                if constexpr (CV) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_l), 32 + 2 * t));
+                else return 1.f;
+            };
+            float kv[CPL][16];   // k (normalised) in fp32, for both passes
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 float kt[CPL], qt[CPL];
+                const float iq = inv_q(t), ik = inv_k(t);
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     a[j][t] = fast_exp2(clamp_log_decay(val(rg[t], fsg, t, j)) * kLog2e);
                     F[j] = t == 0 ? a[j][0] : F[j] * a[j][t];
-                    kt[j] = -(val(rk[t], fsk, t, j) * F[j]);   // stored negated: -K e^G
-                    qt[j] = val(rq[t], fsq, t, j) * F[j];
+                    kv[j][t] = CV ? val(rk[t], fsk, t, j) * ik : val(rk[t], fsk, t, j);
+                    kt[j] = -(kv[j][t] * F[j]);   // stored negated: -K e^G
+                    qt[j] = (CV ? val(rq[t], fsq, t, j) * iq : val(rq[t], fsq, t, j)) * F[j];
                 }
                 wkt[t] = pack(kt);
                 wqt[t] = pack(qt);
+                if constexpr (CV) {   // (stored at once: fewer registers live)
+                    put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
+                    put(slot + Cfg::O_QT + t * PK + pos * 2, wqt[t]);
+                }
             }
             float E[CPL];
 #pragma unroll
@@ -492,9 +723,10 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     if (t < 15) E[j] *= a[j][t + 1];
-                    ki[j] = val(rk[t], fsk, t, j) * E[j];
+                    ki[j] = kv[j][t] * E[j];
                 }
                 wki[t] = pack(ki);
+                if constexpr (CV) put(slot + Cfg::O_KI + t * PH + c0 * 2, wki[t]);
             }
             // beta to fp32 before the next chunk's loads reuse its registers
             // (a conversion sunk below them would keep both copies live and
@@ -502,12 +734,13 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
             float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
             asm volatile("" : "+v"(bl));
             // ---- into the slot -----------------------------------------------
-            char* slot = smem + s * SLOT;
+            if constexpr (!CV) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
-                put(slot + Cfg::O_QT + t * PK + pos * 2, wqt[t]);
-                put(slot + Cfg::O_KI + t * PH + c0 * 2, wki[t]);
+                for (int t = 0; t < 16; ++t) {
+                    put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
+                    put(slot + Cfg::O_QT + t * PK + pos * 2, wqt[t]);
+                    put(slot + Cfg::O_KI + t * PH + c0 * 2, wki[t]);
+                }
             }
             // e^{G_15} per channel, laid out for the consumers' row
             // broadcasts: channel 16*kt + 4*q + i -> entry [q][2*kt + i/2][i%2]
@@ -532,8 +765,10 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
                     rv[h] = bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
                 }
             }
-            *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
-            *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
+            if constexpr (!CV) {
+                *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
+                *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
+            }
             // the next chunk of this wave streams in from here on
             issue_gkq(ci + kNP);
             issue_v(ci + kNP);
@@ -726,21 +961,22 @@ chunk_pipe_kernel(const typename PipeIn<MX>::type* __restrict__ q,
     }
 }
 
-template <int DK, int DVS, bool MX>
+template <int DK, int DVS, int IN>
 hipError_t launch_pipe_t(const void* q, const void* k, const void* v, int64_t stride,
                          const void* g, const void* beta, void* o, const float* s0, float* sT,
                          const int32_t* cu, int num_seqs, int T_len, int H, int DV,
                          const void* qsc, const void* ksc, const void* vsc, const void* gsc,
-                         hipStream_t s) {
-    using TIn = typename PipeIn<MX>::type;
+                         const float* cw, const void* cs_in, float l2_eps, hipStream_t s) {
+    using TIn = typename PipeIn<IN>::type;
     const int nsplit = DV / DVS;
     const int64_t blocks = (int64_t)num_seqs * H * nsplit;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS, MX>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS, IN>), dim3((unsigned)blocks),
                        dim3(PipeCfg<DK, DVS>::THREADS), 0, s, (const TIn*)q, (const TIn*)k,
                        (const TIn*)v, stride, (const TIn*)g, (const __bf16*)beta, (__bf16*)o,
                        s0, sT, cu, num_seqs, T_len, H, DV, nsplit, (const uint8_t*)qsc,
-                       (const uint8_t*)ksc, (const uint8_t*)vsc, (const uint8_t*)gsc);
+                       (const uint8_t*)ksc, (const uint8_t*)vsc, (const uint8_t*)gsc, cw,
+                       (const __bf16*)cs_in, l2_eps, (IN == kInMx || num_seqs > 1) ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -751,10 +987,12 @@ hipError_t launch_chunk_pipe(const void* q, const void* k, const void* v, int64_
                              float* sT, const int32_t* cu, int num_seqs, int T, int H, int DK,
                              int DV, hipStream_t s) {
     if (DK == 128)
-        return launch_pipe_t<128, 64, false>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T,
-                                             H, DV, nullptr, nullptr, nullptr, nullptr, s);
-    return launch_pipe_t<64, 64, false>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
-                                        DV, nullptr, nullptr, nullptr, nullptr, s);
+        return launch_pipe_t<128, 64, kInBf16>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs,
+                                               T, H, DV, nullptr, nullptr, nullptr, nullptr,
+                                               nullptr, nullptr, 0.f, s);
+    return launch_pipe_t<64, 64, kInBf16>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
+                                          DV, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                          0.f, s);
 }
 
 hipError_t launch_chunk_pipe_mxfp8(const void* q, const void* qsc, const void* k,
@@ -762,8 +1000,23 @@ hipError_t launch_chunk_pipe_mxfp8(const void* q, const void* qsc, const void* k
                                    int64_t stride, const void* g, const void* gsc,
                                    const void* beta, void* o, const float* s0, float* sT,
                                    const int32_t* cu, int num_seqs, int T, int H, hipStream_t s) {
-    return launch_pipe_t<128, 64, true>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
-                                        128, qsc, ksc, vsc, gsc, s);
+    return launch_pipe_t<128, 64, kInMx>(q, k, v, stride, g, beta, o, s0, sT, cu, num_seqs, T, H,
+                                         128, qsc, ksc, vsc, gsc, nullptr, nullptr, 0.f, s);
+}
+
+hipError_t launch_chunk_pipe_conv(const void* x, const float* cw, const void* cs_in,
+                                  const void* g, const void* beta, void* o, const float* s0,
+                                  float* sT, const int32_t* cu, int num_seqs, int T, int H, int D,
+                                  float l2_eps, hipStream_t s) {
+    const int64_t HD = (int64_t)H * D;
+    const __bf16* xb = static_cast<const __bf16*>(x);
+    if (D == 128)
+        return launch_pipe_t<128, 64, kInConv>(xb, xb + HD, xb + 2 * HD, 3 * HD, g, beta, o, s0,
+                                               sT, cu, num_seqs, T, H, D, nullptr, nullptr,
+                                               nullptr, nullptr, cw, cs_in, l2_eps, s);
+    return launch_pipe_t<64, 64, kInConv>(xb, xb + HD, xb + 2 * HD, 3 * HD, g, beta, o, s0, sT,
+                                          cu, num_seqs, T, H, D, nullptr, nullptr, nullptr,
+                                          nullptr, cw, cs_in, l2_eps, s);
 }
 
 }  // namespace kda

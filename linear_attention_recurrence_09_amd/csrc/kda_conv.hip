@@ -417,6 +417,23 @@ hipError_t launch_conv_t(const void* x, const float* w, void* y, const void* sta
 
 }  // namespace
 
+hipError_t launch_conv_state(const void* x, const void* state_in, void* state_out,
+                             const int32_t* cu, int num_seqs, int T, int64_t N, int H, int D,
+                             int dtype, hipStream_t s) {
+    if (state_out == nullptr || num_seqs == 0) return hipSuccess;
+    const int P = 3 * H * D;
+    const unsigned sblocks = (unsigned)((P + kConvChannels - 1) / kConvChannels);
+    if (dtype == 0)
+        hipLaunchKernelGGL((conv_state_kernel<float>), dim3((unsigned)num_seqs, sblocks),
+                           dim3(kConvThreads), 0, s, (const float*)x, (const float*)state_in,
+                           (float*)state_out, cu, T, N, P);
+    else
+        hipLaunchKernelGGL((conv_state_kernel<__bf16>), dim3((unsigned)num_seqs, sblocks),
+                           dim3(kConvThreads), 0, s, (const __bf16*)x, (const __bf16*)state_in,
+                           (__bf16*)state_out, cu, T, N, P);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv(const void* x, const float* w, void* y, const void* state_in,
                        void* state_out, const int32_t* cu, int num_seqs, int T, int64_t N,
                        int H, int D, int dtype, float l2_eps, hipStream_t s) {

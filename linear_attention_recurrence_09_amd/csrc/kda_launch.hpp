@@ -59,6 +59,20 @@ hipError_t launch_chunk(const ChunkPlan& plan, const void* q, const void* k, con
                         const float* s0, float* sT, const int32_t* cu, int num_seqs, int T,
                         int H, int DK, int DV, int dtype, hipStream_t s);
 
+// The 16-token kernel reading the projected inputs before the short conv:
+// x [N, 3*H*D] bf16 (q | k | v parts), conv taps cw [3*H*D, 4] fp32, conv
+// state cs_in [num_seqs, 3*H*D, 3] bf16 or null; the producers run conv,
+// SiLU and L2 (kda_chunk_pipe.hip).  D = 64 or 128; o [N, H, D] bf16.
+hipError_t launch_chunk_pipe_conv(const void* x, const float* cw, const void* cs_in,
+                                  const void* g, const void* beta, void* o, const float* s0,
+                                  float* sT, const int32_t* cu, int num_seqs, int T, int H, int D,
+                                  float l2_eps, hipStream_t s);
+
+// The rolling conv state alone (the state pass of kda_conv, kda_conv.hip).
+hipError_t launch_conv_state(const void* x, const void* state_in, void* state_out,
+                             const int32_t* cu, int num_seqs, int T, int64_t N, int H, int D,
+                             int dtype, hipStream_t s);
+
 // Gated latent-attention decode step (kda_mla.hip): bf16, latent 512, heads of
 // 128, H a multiple of 16 up to 96.
 int mla_splits(int B, int Lmax);

@@ -34,7 +34,7 @@ def test_header_declares_the_calls():
                           "kda_conv_mxfp8", "kda_decode_multi", "kda_decode_step",
                           "kda_gated_norm", "kda_last_error", "kda_mla_decode",
                           "kda_mla_decode_noalloc", "kda_mla_decode_workspace_bytes",
-                          "kda_version"]
+                          "kda_prefill_fused", "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -251,3 +251,35 @@ def test_mla_decode_noalloc_argument_checks(L):
     assert L.kda_mla_decode_workspace_bytes(4096, 96, 64) > cap
     assert na(B=4096, Lm=64) == INVALID
     assert "static scratch" in kda.kda_last_error()
+
+
+def test_prefill_fused_argument_checks(L):
+    """The fused prefill refuses bad requests on the host (no HIP call)."""
+    H, D, T = 2, 128, 64
+    N, P = T, 3 * H * D
+    xb, tb = N * P * 2, N * H * D * 2
+
+    def fused(x=A, w=A + 8 * MB, g=A + 9 * MB, b=A + 10 * MB, z=A + 11 * MB, nw=A + 12 * MB,
+              o=A + 13 * MB, y=A + 14 * MB, csi=None, cso=None, s0=None, sT=None, cu=None, ns=0,
+              B=1, T=T, H=H, D=D, dt=1, l2=1e-6, rms=1e-6):
+        return L.kda_prefill_fused(x, w, g, b, z, nw, o, y, csi, cso, s0, sT, cu, ns, B, T, H, D,
+                                   dt, ctypes.c_float(l2), ctypes.c_float(rms), None)
+    assert xb < 8 * MB and tb < MB
+    assert fused(x=None) == INVALID
+    assert fused(y=None) == INVALID
+    assert fused(dt=0) == UNSUPPORTED                        # bf16 only
+    assert fused(dt=5) == INVALID
+    assert fused(D=96) == UNSUPPORTED
+    assert fused(H=0) == INVALID
+    assert fused(l2=0.0) == INVALID
+    assert fused(rms=-1.0) == INVALID
+    assert fused(T=-1) == INVALID
+    assert fused(o=A + 13 * MB + 8) == INVALID               # misaligned
+    assert fused(o=A + 16) == INVALID                        # o over x
+    assert fused(y=A + 9 * MB) == INVALID                    # y over g
+    assert fused(y=A + 13 * MB + 64) == INVALID              # y partly over o
+    assert fused(s0=A + 15 * MB, sT=A + 15 * MB + 64) == INVALID   # partial state alias
+    assert fused(csi=A + 20 * MB, cso=A + 20 * MB + 32) == INVALID
+    assert fused(cu=A + 30 * MB, B=2) == INVALID             # offsets need B = 1
+    assert "kda_prefill_fused" in kda.kda_last_error()
+    assert fused(B=0) == OK                                  # nothing to do
