@@ -493,6 +493,8 @@ def main():
         # the MXFP8 step on the same inputs, three times (conv, chunk, norm)
         bench_mxfp8_prefill(kda, synth, torch, stream, x, w, g, beta, gate, nw, H, D, steps=3,
                             warmup=0)
+        # the fused prefill on the same inputs, three times
+        bench_fused_prefill(kda, torch, stream, x, w, g, beta, gate, nw, H, D, steps=3, warmup=0)
         # the decode kernels: three one-token steps, two calls of four tokens
         dspec = synth.CONFIGS[4]
         Bd, Hd, Dd = dspec.B, dspec.H, dspec.D
@@ -516,7 +518,8 @@ def main():
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        log("counter run done: conv, 3 chunk launches, norm, 3 MXFP8 prefill steps, 3 decode "
+        log("counter run done: conv, 3 chunk launches, norm, 3 MXFP8 prefill steps, 3 fused "
+            "prefill steps, 3 decode "
             "steps, 2 four-token decode calls, 6 latent-attention decode steps, 3 copies of "
             "2 GiB")
         return

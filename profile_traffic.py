@@ -30,10 +30,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 COPY_BYTES = 2 * 1024 ** 3
-# mangled names as rocprofv3 -T prints them: the bf16 and the MXFP8
-# instantiation of the 16-token chunk kernel (template flag b0 / b1)
-CHUNK_TAG = "chunk_pipe_kernelILi128ELi64ELb0E"
-MX_TAG = "chunk_pipe_kernelILi128ELi64ELb1E"
+# mangled names as rocprofv3 -T prints them: the bf16, MXFP8 and fused-conv
+# instantiations of the 16-token chunk kernel (input-mode template argument
+# 0 / 1 / 2)
+CHUNK_TAG = "chunk_pipe_kernelILi128ELi64ELi0E"
+MX_TAG = "chunk_pipe_kernelILi128ELi64ELi1E"
+CV_TAG = "chunk_pipe_kernelILi128ELi64ELi2E"
 COPY_TAG = "vectorized_elementwise_kernel"
 
 
@@ -191,6 +193,7 @@ def main():
          bench.mxfp8_conv_bytes(65536, 96, 128)),
         ("chunk MXFP8 (kda_chunk_prefill_mxfp8, T=65536)", MX_TAG,
          bench.mxfp8_chunk_bytes(65536, 96, 128, 1)),
+        ("fused conv+chunk (kda_prefill_fused, T=65536)", CV_TAG, pb["chunk"]),
         ("gated norm (kda_gated_norm, T=65536)", "gated_norm_kernel", pb["norm"]),
         ("decode, 1 token (kda_decode_step, B=256)", "decode_multi_kernelIDF16bLi128ELb1",
          bench.decode_bytes(256, 96, 128)),
