@@ -50,6 +50,18 @@
 // values; V codes are decoded the same way and stored to the slot as bf16
 // (exact).  Everything after that is the bf16 kernel's code, so on the
 // decoded values both give bitwise equal results.
+//
+// Conv inputs ("Inside Kimi K3", KDA short-convolution diagram and one-head
+// diagram).  A third instantiation reads the projected inputs before the
+// short convolution.  Each producer runs the 4-tap causal conv and SiLU on its
+// lane's two channels of q and k over the chunk's 16 tokens (the 3 rows
+// before the chunk come from the input, or on a sequence's first chunk from
+// the incoming rolling state) and on a 2-column x 8-token patch of the
+// workgroup's V slice.  The squares of a token's q (k) values are summed
+// across the wave by a transposing butterfly that leaves lane l holding the
+// sum of one (token, part) pair; its inverse square root is broadcast by
+// readlane where q and k are scaled.  From the decay products on it is the
+// bf16 kernel's code.
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -560,16 +572,25 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         for (int64_t ci = pw; ci < n_chunks;) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
-            const bool go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+            // The slot is waited for before the chunk's work, except with MXFP8
+            // or conv inputs: there the decoding (or the convolution) and the
+            // decay products are worked up in registers first and only the
+            // slot writes wait, which takes that work off the hand-over's
+            // critical path (measured faster for both; the bf16 instantiation
+            // measured no faster with the wait last)
+            constexpr bool kLateWait = MX || CV;
+            bool go = kLateWait ? true : wait_all_at_least<NC>(&released[s * NC], round, stop);
             char* slot = smem + s * SLOT;
 
             // ---- conv inputs: short conv, SiLU, L2 of q and k ------------------
             // ("Inside Kimi K3", KDA short-convolution diagram: 4 taps per
             // channel over x_{t-3} .. x_t, then SiLU; KDA one-head diagram: L2
-            // norm of q and k.)  V goes to the slot in bf16; q and k stay in
-            // rq / rk as bf16 words before the norm, and inv_l holds the
-            // inverse norm of (token, part) = (l/2 % 16, l/32) for lane l
+            // norm of q and k.)  V stays in vw as bf16 words until the slot is
+            // free; q and k stay in rq / rk as bf16 words before the norm, and
+            // inv_l holds the inverse norm of (token, part) = (l/2 % 16, l/32)
+            // for lane l
             float inv_l = 1.f;
+            uint32_t vw[CV ? 8 : 1];
             if constexpr (CV) {
                 const float* wl = reinterpret_cast<const float*>(smem + O_W);
                 // on the first chunk the 3 rows before it come from the state
@@ -604,8 +625,7 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                         for (int j = 0; j < 2; ++j)
                             y[j] = siluf_(w[j][0] * xv(t, j) + w[j][1] * xv(t + 1, j) +
                                           w[j][2] * xv(t + 2, j) + w[j][3] * xv(t + 3, j));
-                        *reinterpret_cast<uint32_t*>(slot + Cfg::O_V + (8 * hv + t) * Cfg::PV + cp * 4) =
-                            __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{y[0], y[1]}, bf16x2));
+                        vw[t] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{y[0], y[1]}, bf16x2));
                     }
                 }
                 // q and k: conv + SiLU per channel, squares summed per token
@@ -709,10 +729,6 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 }
                 wkt[t] = pack(kt);
                 wqt[t] = pack(qt);
-                if constexpr (CV) {   // (stored at once: fewer registers live)
-                    put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
-                    put(slot + Cfg::O_QT + t * PK + pos * 2, wqt[t]);
-                }
             }
             float E[CPL];
 #pragma unroll
@@ -726,15 +742,27 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                     ki[j] = kv[j][t] * E[j];
                 }
                 wki[t] = pack(ki);
-                if constexpr (CV) put(slot + Cfg::O_KI + t * PH + c0 * 2, wki[t]);
             }
             // beta to fp32 before the next chunk's loads reuse its registers
             // (a conversion sunk below them would keep both copies live and
             // add a register move that waits for the loads)
             float bl = __builtin_bit_cast(float, rbl << 16);   // bf16 -> fp32
             asm volatile("" : "+v"(bl));
+            if constexpr (kLateWait) {
+                // (the empty asm keeps the work above on this side of the
+                // wait: the compiler would otherwise sink it to its uses)
+#pragma unroll
+                for (int t = 0; t < 16; ++t) asm volatile("" : "+v"(wkt[t]), "+v"(wqt[t]), "+v"(wki[t]));
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) asm volatile("" : "+v"(F[j]));
+                if constexpr (CV) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(vw[t]));
+                }
+                go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+            }
             // ---- into the slot -----------------------------------------------
-            if constexpr (!CV) {
+            {
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
                     put(slot + Cfg::O_KT + t * PK + pos * 2, wkt[t]);
@@ -768,6 +796,10 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
             if constexpr (!CV) {
                 *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2) = rv[0];
                 *reinterpret_cast<bf16x8*>(slot + Cfg::O_V + vt * Cfg::PV + vc * 2 + 16) = rv[1];
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    *reinterpret_cast<uint32_t*>(slot + Cfg::O_V + (8 * hv + t) * Cfg::PV + cp * 4) = vw[t];
             }
             // the next chunk of this wave streams in from here on
             issue_gkq(ci + kNP);
