@@ -89,3 +89,34 @@ def test_ragged_tail_block_and_empty():
         report("o", gpu, ref, TOL["bf16"])
     e = np.zeros((0, 2, 4))
     assert report("empty", e, e, TOL["bf16"]) == 0.0
+
+
+def test_mxfp8_code_window_bounds_an_fp32_evaluation():
+    """The per-element error bound that widens the MXFP8 code check's ties
+    (tests/test_gpu_mxfp8._error_bound) covers an fp32 evaluation of conv,
+    SiLU and L2 against the fp64 oracle, with room to spare, and is not
+    vacuous (far below the values themselves)."""
+    import torch
+    from oracle import c_oracle, kda_ref
+    from tests.test_gpu_mxfp8 import _error_bound
+    rng = np.random.default_rng(0)
+    H, D, N = 3, 128, 300
+    P = 3 * H * D
+    xs = torch.from_numpy(rng.standard_normal((N, P))).to(torch.bfloat16).double().numpy()
+    ws = (rng.standard_normal((P, 4)) * 0.25).astype(np.float32).astype(np.float64)
+    ys, _ = c_oracle.short_conv_silu(xs, ws, None)
+    u_pre = ys.reshape(N, 3, H, D)
+    ref = u_pre.copy()
+    ref[:, :2] = kda_ref.l2norm(ref[:, :2])
+    err = _error_bound(xs, ws, None, [0, N], u_pre)
+    x32, w32 = xs.astype(np.float32), ws.astype(np.float32)
+    xp = np.concatenate([np.zeros((3, P), np.float32), x32], 0)
+    pre = np.zeros((N, P), np.float32)
+    for j in range(4):
+        pre = (pre + w32[:, j] * xp[j:j + N]).astype(np.float32)
+    u = (pre / (np.float32(1) + np.exp(-pre))).astype(np.float32).reshape(N, 3, H, D)
+    ss = np.square(u[:, :2]).sum(-1, keepdims=True, dtype=np.float32)
+    y32 = u.copy()
+    y32[:, :2] = u[:, :2] * (np.float32(1) / np.sqrt(ss + np.float32(1e-6)))
+    assert np.all(np.abs(y32 - ref) <= 0.5 * err)
+    assert np.median(err / np.maximum(np.abs(ref), 1e-30)) < 1e-4
