@@ -180,9 +180,13 @@ template <int M>
 __device__ __forceinline__ void back_subst_split_steps(float (&y)[4], const float (&np)[4],
                                                        int lr) {
     if constexpr (M >= 1) {
-        const float piv = __builtin_bit_cast(
-            float, __builtin_amdgcn_ds_bpermute(((M & 3) * 16 + lr) * 4,
-                                                __builtin_bit_cast(int, y[M / 4])));
+        // row M % 4 to all four rows: a 16-lane swap picks its row's pair,
+        // a 32-lane swap its half (two VALU operations, no LDS round trip)
+        const unsigned x = __builtin_bit_cast(unsigned, y[M / 4]);
+        const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        const unsigned ah = (M & 1) ? a[1] : a[0];
+        const auto b = __builtin_amdgcn_permlane32_swap(ah, ah, false, false);
+        const float piv = __builtin_bit_cast(float, (M & 2) ? b[1] : b[0]);
 #pragma unroll
         for (int k = 0; k < (M + 3) / 4; ++k) fmac_bcast<M>(y[k], np[k], piv);
         back_subst_split_steps<M - 1>(y, np, lr);
@@ -801,9 +805,13 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 for (int t = 0; t < 8; ++t)
                     *reinterpret_cast<uint32_t*>(slot + Cfg::O_V + (8 * hv + t) * Cfg::PV + cp * 4) = vw[t];
             }
-            // the next chunk of this wave streams in from here on
-            issue_gkq(ci + kNP);
-            issue_v(ci + kNP);
+            // the next chunk of this wave streams in from here on (with the
+            // slot wait last, from the end of this chunk: the loads then stay
+            // off the path from the slot's release to its publication)
+            if constexpr (!kLateWait) {
+                issue_gkq(ci + kNP);
+                issue_v(ci + kNP);
+            }
 
             // ---- A_kk^T, A_qk^T (16x16x32 MFMA over the key channels) -------
             floatx4 akk = zero4(), aqk = zero4();
@@ -858,6 +866,10 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 if (lane == 0)
                     __hip_atomic_store(&ready[s], round + 1, __ATOMIC_RELEASE,
                                        __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            if constexpr (kLateWait) {
+                issue_gkq(ci + kNP);
+                issue_v(ci + kNP);
             }
             ci = go ? ci + kNP : n_chunks;
         }
