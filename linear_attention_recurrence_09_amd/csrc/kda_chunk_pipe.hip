@@ -25,8 +25,9 @@
 //    each lane holding all 16 tokens of its channels, the operand tiles -Kt,
 //    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  Each 16 x 16
 //    unit triangular inverse is solved by back substitution in registers
-//    (row broadcasts by DPP) by the chunk's own producer, so a chunk never
-//    waits for another producer.  Results go to a ring of LDS slots.
+//    (broadcasts within a 16-lane row by DPP, across rows by permlane swaps)
+//    by the chunk's own producer, so a chunk never waits for another
+//    producer.  Results go to a ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
 //    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
@@ -104,8 +105,9 @@ struct PipeCfg {
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    // triangular-inverse scratch, one per slot: the 16 columns of -N (16
-    // floats each) and beta of the slot's chunk
+    // triangular-inverse scratch, one per slot (used with conv inputs; the
+    // other instantiations move these values with permlane swaps): the 16
+    // columns of -N (16 floats each) and beta of the slot's chunk
     static constexpr int O_NB = kRing * SLOT;
     static constexpr int O_BT = O_NB + kRing * 16 * 16 * 4;
     static constexpr int BYTES = O_BT + kRing * 16 * 4;
@@ -164,14 +166,37 @@ __device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
                  : "v"(n), "v"(m), "i"(M));
 }
 
+// Row exchanges between two registers (gfx950 permlane swaps; both registers
+// are read and written): swap32 trades rows 2, 3 of a for rows 0, 1 of b,
+// swap16 the odd rows of a for the even rows of b.  Written as asm: the
+// compiler's builtin lost the second register's result when the two operands
+// differed.  The s_nops give the swaps their VALU read and write wait states.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// Lane c of row q of x, for every row q: row R of x broadcast to all four
+// 16-lane rows (R compile-time).
+template <int R>
+__device__ __forceinline__ float rows_bcast(float x) {
+    float a = x, b = x;
+    swap16(a, b);                 // a: rows 0, 0, 2, 2   b: rows 1, 1, 3, 3
+    float c = (R & 1) ? b : a, d = c;
+    swap32(c, d);                 // c: rows (R&1) twice   d: rows 2 + (R&1) twice
+    return (R & 2) ? d : c;
+}
+
 // Back substitution for Y = (I + N)^{-1}, N strictly upper triangular, split
 // over the four 16-lane rows (one chunk per wave): with Y - I = -N - N(Y - I)
 // solved column by column, entry M of a column is final once the entries
 // above it are done, and it updates every row r < M with -N[r][M].  Lane c
 // of row q holds rows r = q + 4k (k = 0..3) of column c, of -N in np[k] and
 // of Y in y[k] (started at column c of I, so Y comes out with its diagonal).
-// Step M fetches the finished entry Y[M][c] from its owner row (M % 4, slot
-// M / 4; one ds_bpermute) and updates the slots k < ceil(M / 4) of every row:
+// Step M broadcasts the finished entry Y[M][c] from its owner row (M % 4,
+// slot M / 4; two permlane swaps) and updates the slots k < ceil(M / 4) of
+// every row:
 // the rows r >= M among them add -N[r][M] = 0 (the masked entries are stored
 // as zeros).  36 broadcast multiply-adds in all.  np is complete before the
 // first broadcast read (the s_nop consumes it and adds the DPP read wait
@@ -180,13 +205,8 @@ template <int M>
 __device__ __forceinline__ void back_subst_split_steps(float (&y)[4], const float (&np)[4],
                                                        int lr) {
     if constexpr (M >= 1) {
-        // row M % 4 to all four rows: a 16-lane swap picks its row's pair,
-        // a 32-lane swap its half (two VALU operations, no LDS round trip)
-        const unsigned x = __builtin_bit_cast(unsigned, y[M / 4]);
-        const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-        const unsigned ah = (M & 1) ? a[1] : a[0];
-        const auto b = __builtin_amdgcn_permlane32_swap(ah, ah, false, false);
-        const float piv = __builtin_bit_cast(float, (M & 2) ? b[1] : b[0]);
+        // row M % 4 to all four rows (two permlane swaps, no LDS round trip)
+        const float piv = rows_bcast<M & 3>(y[M / 4]);
 #pragma unroll
         for (int k = 0; k < (M + 3) / 4; ++k) fmac_bcast<M>(y[k], np[k], piv);
         back_subst_split_steps<M - 1>(y, np, lr);
@@ -837,29 +857,53 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
             // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk ------------------------
             // Column c = lr of -N holds -beta_c A_kk[c][r] for r < c; lane
             // (q, c) has rows r = 4q+i (the tile holds -Kt, so akk[i] =
-            // -A_kk[c][4q+i]).  It goes through this slot's scratch, with beta,
-            // to the column layout of the solve, which the four lane rows share
-            // (see back_subst_split); each row then writes its rows of M'.
-            float* col = reinterpret_cast<float*>(smem + Cfg::O_NB) + (s * 16 + lr) * 16;
-            float* bet = reinterpret_cast<float*>(smem + Cfg::O_BT) + s * 16;
-            *reinterpret_cast<floatx4*>(col + 4 * lq) =
-                floatx4{4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
-                        4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
-            if (lq == 0) bet[lr] = bl;
-            if (go) {
-                float np[4], y[4];
+            // -A_kk[c][4q+i]).  The solve wants lane row q to hold rows q + 4k
+            // (k = 0..3) of the column (see back_subst_split), and each row
+            // then writes its rows of M', scaled by beta_{4k+q}.
+            float np[4] = {4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
+                           4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
+            float bk[4];
+            if constexpr (CV) {
+                // conv inputs (fewer registers to spare): through this slot's
+                // scratch in LDS, with beta
+                float* col = reinterpret_cast<float*>(smem + Cfg::O_NB) + (s * 16 + lr) * 16;
+                float* bet = reinterpret_cast<float*>(smem + Cfg::O_BT) + s * 16;
+                *reinterpret_cast<floatx4*>(col + 4 * lq) = floatx4{np[0], np[1], np[2], np[3]};
+                if (lq == 0) bet[lr] = bl;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     np[k] = col[lq + 4 * k];
-                    y[k] = lq + 4 * k == lr ? 1.f : 0.f;
+                    bk[k] = bet[4 * k + lq];
                 }
+            } else {
+                // a 4 x 4 transpose of (lane row, slot) in two rounds of
+                // permlane swaps; beta_{4k+q} as lane 4a+q of each quad a (a
+                // quad permutation on row q alone), then lane 4k of the row
+                swap32(np[0], np[2]);
+                swap32(np[1], np[3]);
+                swap16(np[0], np[1]);
+                swap16(np[2], np[3]);
+                float bq = 0.f;
+                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0x00, 0x1, 0xF, false));
+                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0x55, 0x2, 0xF, false));
+                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0xAA, 0x4, 0xF, false));
+                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0xFF, 0x8, 0xF, false));
+                bk[0] = row_bcast<0>(bq);
+                bk[1] = row_bcast<4>(bq);
+                bk[2] = row_bcast<8>(bq);
+                bk[3] = row_bcast<12>(bq);
+            }
+            if (go) {
+                float y[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) y[k] = lq + 4 * k == lr ? 1.f : 0.f;
                 back_subst_split(y, np, lr);
                 // M'[lr][4k+q] = Y[4k+q][lr] beta_{4k+q}: entry q of the
                 // 4-entry group k of lane (k, lr) of the 16x16x16 A operand
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
                     *reinterpret_cast<__bf16*>(slot + Cfg::O_MP + (16 * k + lr) * 8 + lq * 2) =
-                        (__bf16)(y[k] * bet[4 * k + lq]);
+                        (__bf16)(y[k] * bk[k]);
                 // publish the chunk after every lane's M' writes (the LDS
                 // performs this wave's operations in order; the release keeps
                 // the compiler from sinking the writes below it)
