@@ -170,12 +170,14 @@ __device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
 // are read and written): swap32 trades rows 2, 3 of a for rows 0, 1 of b,
 // swap16 the odd rows of a for the even rows of b.  Written as asm: the
 // compiler's builtin lost the second register's result when the two operands
-// differed.  The s_nops give the swaps their VALU read and write wait states.
+// differed.  The s_nop gives a swap the wait states after the VALU write of
+// its operands (its results need none: the compiler's own swaps are read at
+// once).
 __device__ __forceinline__ void swap32(float& a, float& b) {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 __device__ __forceinline__ void swap16(float& a, float& b) {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 // Lane c of row q of x, for every row q: row R of x broadcast to all four
 // 16-lane rows (R compile-time).
