@@ -105,16 +105,22 @@ struct PipeCfg {
     static constexpr int O_AQ = O_MP + 512;             // A_qk as 16x16x16 A operands
     static constexpr int O_GM = O_AQ + 512;             // e^{G15}, consumer lane order
     static constexpr int SLOT = O_GM + 512;
-    // triangular-inverse scratch, one per slot (used with conv inputs; the
-    // other instantiations move these values with permlane swaps): the 16
-    // columns of -N (16 floats each) and beta of the slot's chunk
-    static constexpr int O_NB = kRing * SLOT;
+    static constexpr int RING = kRing * SLOT;
+    // behind the ring, one of two per-slot areas:
+    //  * (conv inputs) the triangular-inverse scratch: the 16 columns of -N
+    //    (16 floats each) and beta of the slot's chunk;
+    //  * (the others, which move those values with permlane swaps) the
+    //    chunk's output rows, 16 tokens x this workgroup's value columns in
+    //    bf16, gathered from the consumers and stored to memory whole
+    static constexpr int O_NB = RING;
     static constexpr int O_BT = O_NB + kRing * 16 * 16 * 4;
-    static constexpr int BYTES = O_BT + kRing * 16 * 4;
+    static constexpr int SCRATCH = kRing * (16 * 16 * 4 + 16 * 4);
+    static constexpr int PO = DVS * 2 + 16;             // output row pitch: rows 36 words apart
+    static constexpr int O_OS = RING;
+    static constexpr int STAGE = kRing * 16 * PO;
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
-    static_assert(BYTES <= 160 * 1024 - 256, "LDS budget");
     // every producer keeps one slot (rings whose size does not divide the
     // producer count gave wrong results in tests)
     static_assert(kNP % kRing == 0, "ring size divides the producer count");
@@ -325,7 +331,7 @@ __device__ __forceinline__ float e8m0_scale(uint32_t s) {
     return __builtin_bit_cast(float, bits);
 }
 
-template <int DK, int DVS, int IN = kInBf16, int THREADS = PipeCfg<DK, DVS>::THREADS>
+template <int DK, int DVS, int IN, bool SO, int THREADS = PipeCfg<DK, DVS>::THREADS>
 __global__ void __launch_bounds__(THREADS)
 chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                   const typename PipeIn<IN>::type* __restrict__ k,
@@ -346,11 +352,20 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
     constexpr int PK = Cfg::PK, PH = Cfg::PH, SLOT = Cfg::SLOT;
     // conv inputs: the workgroup's conv taps (q and k channels of the head,
     // then its value columns), 4 floats each, behind the ring
-    constexpr int O_W = Cfg::BYTES;
+    // Output rows staged in LDS and stored whole by the producers (SO), or
+    // stored by the consumers in 32-byte pieces.  Staged for one sequence of
+    // bf16 inputs, where four consumers writing 32-byte pieces of one 128-byte
+    // line made the workgroups of some heads 7 % slower (per-workgroup
+    // timing; the same rows written whole removed it); direct for packed
+    // batches and MXFP8 inputs (measured faster there) and for conv inputs
+    // (no room for the staging area beside the scratch and the taps)
+    constexpr bool kStageO = SO;
+    static_assert(!SO || !CV, "no output staging with conv inputs");
+    constexpr int O_W = Cfg::RING + (kStageO ? Cfg::STAGE : Cfg::SCRATCH);
     constexpr int WBYTES = CV ? (2 * DK + DVS) * 16 : 0;
-    static_assert(Cfg::BYTES + WBYTES <= 160 * 1024 - 256, "LDS budget (conv taps)");
+    static_assert(O_W + WBYTES <= 160 * 1024 - 256, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES + WBYTES];
+    __shared__ __attribute__((aligned(16))) char smem[O_W + WBYTES];
     // ready[kRing], released[kRing][NC] (one counter per consumer), stop
     constexpr int NFLAGS = kRing + kRing * NC + 1;
     __shared__ __attribute__((aligned(16))) int flags[NFLAGS];
@@ -595,6 +610,23 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         // lets the body run once more on whatever the slot holds, publishes
         // nothing, and ends the loop.
         const int pos = perm_pos(c0);   // this lane's channels in the permuted tiles
+        // The output rows of chunk c, gathered in the slot's staging area by
+        // the four consumers before they released the slot: lane l stores 32
+        // bytes of row l / 4, so each row of the workgroup's value columns is
+        // written whole; rows past the sequence end fall outside the resource.
+        auto store_o = [&](int64_t c, int s_c) {
+            int64_t t0;
+            const int valid = chunk_rows(c, t0);
+            const int o_row = H * DV * 2;
+            const char* st = smem + Cfg::O_OS + s_c * 16 * Cfg::PO + (lane >> 2) * Cfg::PO + (lane & 3) * 32;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(st);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(st + 16);
+            const rsrc_t r_o = make_rsrc(o + (t0 * H + head) * DV + n0, (uint32_t)(valid * o_row));
+            const int off = (lane >> 2) * o_row + (lane & 3) * 32;
+            __builtin_amdgcn_raw_buffer_store_b128(a, r_o, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(b, r_o, off + 16, 0, 0);
+        };
+        int64_t last = -1;               // the last chunk this wave published
         for (int64_t ci = pw; ci < n_chunks;) {
             const int s = (int)(ci % kRing);
             const int round = (int)(ci / kRing);
@@ -607,6 +639,11 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
             constexpr bool kLateWait = MX || CV;
             bool go = kLateWait ? true : wait_all_at_least<NC>(&released[s * NC], round, stop);
             char* slot = smem + s * SLOT;
+            // every consumer has released the slot's previous chunk, so its
+            // output rows are complete in the staging area
+            if constexpr (kStageO && !kLateWait) {
+                if (go && ci >= kRing) store_o(ci - kRing, s);
+            }
 
             // ---- conv inputs: short conv, SiLU, L2 of q and k ------------------
             // ("Inside Kimi K3", KDA short-convolution diagram: 4 taps per
@@ -786,6 +823,9 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                     for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(vw[t]));
                 }
                 go = wait_all_at_least<NC>(&released[s * NC], round, stop);
+                if constexpr (kStageO) {
+                    if (go && ci >= kRing) store_o(ci - kRing, s);
+                }
             }
             // ---- into the slot -----------------------------------------------
             {
@@ -917,7 +957,17 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 issue_gkq(ci + kNP);
                 issue_v(ci + kNP);
             }
+            if (go) last = ci;
             ci = go ? ci + kNP : n_chunks;
+        }
+        // the output rows of this wave's last chunk, once every consumer has
+        // released it (a wait that runs out leaves them unwritten; the final
+        // state then reads NaN)
+        if constexpr (kStageO) {
+            if (last >= 0) {
+                const int s = (int)(last % kRing);
+                if (wait_all_at_least<NC>(&released[s * NC], (int)(last / kRing) + 1, stop)) store_o(last, s);
+            }
         }
         return;
     }
@@ -1019,7 +1069,14 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         // O^T += U^T A_qk^T: U's accumulator is the A operand of U^T, and the
         // A_qk operand registers are the B operand of A_qk^T
         oa = mfma16(ub, aq, oa);
-        // every read of this slot has been issued; the release waits for them
+        // lane (q, t) holds O[t][16w + 4q .. +3]: 8 bytes of the chunk's output
+        // rows, staged for the producer that refills this slot
+        if constexpr (kStageO)
+            *reinterpret_cast<u32x2*>(smem + Cfg::O_OS + (ci % kRing) * 16 * Cfg::PO + lr * Cfg::PO +
+                                      (16 * w + 4 * lq) * 2) =
+                __builtin_bit_cast(u32x2, pack4(oa[0], oa[1], oa[2], oa[3]));
+        // every read of this slot (and the staging write) has been issued; the
+        // release waits for them
         flag_store(&released[(ci % kRing) * NC + w], (int)(ci / kRing) + 1, lane);
         // the next chunk's leading operands, read while the state updates
         ok = __builtin_amdgcn_readfirstlane(peek) >= target || wait_at_least(rdy, target, stop);
@@ -1031,15 +1088,17 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         // row, component i % 2
         decay_rows<0, NKT>(S, gm);
 
-        // lane (q, t) holds O[t][16w + 4q .. +3]: one 8-byte store per lane;
+        // conv inputs: lane (q, t) stores O[t][16w + 4q .. +3] itself, 8 bytes;
         // the resource covers the chunk's rows inside the sequence, so rows
         // past its end are dropped without a branch
-        const rsrc_t r_o = make_rsrc(o_chunk, (uint32_t)((rows_left < 16 ? rows_left : 16) * o_row));
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u32x2, pack4(oa[0], oa[1], oa[2], oa[3])), r_o,
-            lr * o_row + 8 * lq, 0, 0);
-        o_chunk += 16 * H * DV;
-        rows_left -= 16;
+        if constexpr (!kStageO) {
+            const rsrc_t r_o = make_rsrc(o_chunk, (uint32_t)((rows_left < 16 ? rows_left : 16) * o_row));
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(u32x2, pack4(oa[0], oa[1], oa[2], oa[3])), r_o,
+                lr * o_row + 8 * lq, 0, 0);
+            o_chunk += 16 * H * DV;
+            rows_left -= 16;
+        }
         ci = ok ? cn : (unsigned)nch;
     }
     if (sT != nullptr) {
@@ -1061,12 +1120,19 @@ hipError_t launch_pipe_t(const void* q, const void* k, const void* v, int64_t st
     const int nsplit = DV / DVS;
     const int64_t blocks = (int64_t)num_seqs * H * nsplit;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS, IN>), dim3((unsigned)blocks),
-                       dim3(PipeCfg<DK, DVS>::THREADS), 0, s, (const TIn*)q, (const TIn*)k,
-                       (const TIn*)v, stride, (const TIn*)g, (const __bf16*)beta, (__bf16*)o,
-                       s0, sT, cu, num_seqs, T_len, H, DV, nsplit, (const uint8_t*)qsc,
-                       (const uint8_t*)ksc, (const uint8_t*)vsc, (const uint8_t*)gsc, cw,
-                       (const __bf16*)cs_in, l2_eps, (IN == kInMx || num_seqs > 1) ? 1 : 0);
+    const int blocked = (IN == kInMx || num_seqs > 1) ? 1 : 0;
+    auto go = [&](auto so) {
+        hipLaunchKernelGGL((chunk_pipe_kernel<DK, DVS, IN, decltype(so)::value>), dim3((unsigned)blocks),
+                           dim3(PipeCfg<DK, DVS>::THREADS), 0, s, (const TIn*)q, (const TIn*)k,
+                           (const TIn*)v, stride, (const TIn*)g, (const __bf16*)beta, (__bf16*)o,
+                           s0, sT, cu, num_seqs, T_len, H, DV, nsplit, (const uint8_t*)qsc,
+                           (const uint8_t*)ksc, (const uint8_t*)vsc, (const uint8_t*)gsc, cw,
+                           (const __bf16*)cs_in, l2_eps, blocked);
+    };
+    if (IN == kInBf16 && !blocked)
+        go(std::integral_constant<bool, IN == kInBf16>{});
+    else
+        go(std::false_type{});
     return hipGetLastError();
 }
 
