@@ -32,10 +32,11 @@ sys.path.insert(0, ROOT)
 COPY_BYTES = 2 * 1024 ** 3
 # mangled names as rocprofv3 -T prints them: the bf16, MXFP8 and fused-conv
 # instantiations of the 16-token chunk kernel (input-mode template argument
-# 0 / 1 / 2)
-CHUNK_TAG = "chunk_pipe_kernelILi128ELi64ELi0E"
-MX_TAG = "chunk_pipe_kernelILi128ELi64ELi1E"
-CV_TAG = "chunk_pipe_kernelILi128ELi64ELi2E"
+# 0 / 1 / 2; the bool after it is the output staging, on for one sequence of
+# bf16 inputs)
+CHUNK_TAG = "chunk_pipe_kernelILi128ELi64ELi0ELb1E"
+MX_TAG = "chunk_pipe_kernelILi128ELi64ELi1ELb0E"
+CV_TAG = "chunk_pipe_kernelILi128ELi64ELi2ELb0E"
 COPY_TAG = "vectorized_elementwise_kernel"
 
 
