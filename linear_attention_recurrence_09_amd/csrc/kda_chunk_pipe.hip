@@ -36,6 +36,11 @@
 //    accumulator's row order, and -Kt / Qt are stored in LDS in that order.
 //    A consumer reads the next chunk's leading operands while it updates the
 //    state, and issues no global loads (V comes through the slot).
+//  * Output rows.  For one sequence of bf16 inputs the consumers write their
+//    pieces of the chunk's output rows to an LDS staging area beside the
+//    slot, and the producer that refills the slot stores each row whole
+//    (128 bytes of one line); otherwise each consumer stores its 8-byte
+//    pieces itself.
 //  * Slots are handed over through LDS counters (producer: "chunk ready",
 //    each consumer: "slot released"), so producers run ahead of the consumers
 //    by up to the ring depth.  Every wait is bounded; a wait that runs out
@@ -1088,9 +1093,10 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         // row, component i % 2
         decay_rows<0, NKT>(S, gm);
 
-        // conv inputs: lane (q, t) stores O[t][16w + 4q .. +3] itself, 8 bytes;
-        // the resource covers the chunk's rows inside the sequence, so rows
-        // past its end are dropped without a branch
+        // unstaged (packed batches, MXFP8 and conv inputs): lane (q, t) stores
+        // O[t][16w + 4q .. +3] itself, 8 bytes; the resource covers the
+        // chunk's rows inside the sequence, so rows past its end are dropped
+        // without a branch
         if constexpr (!kStageO) {
             const rsrc_t r_o = make_rsrc(o_chunk, (uint32_t)((rows_left < 16 ? rows_left : 16) * o_row));
             __builtin_amdgcn_raw_buffer_store_b64(
