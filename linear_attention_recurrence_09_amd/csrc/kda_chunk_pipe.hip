@@ -23,11 +23,11 @@
 //  * Producer waves (8, two per SIMD) build everything that does not depend
 //    on the state, one whole chunk per wave: per-channel decay products with
 //    each lane holding all 16 tokens of its channels, the operand tiles -Kt,
-//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  Each 16 x 16
-//    unit triangular inverse is solved by back substitution in registers
-//    (broadcasts within a 16-lane row by DPP, across rows by permlane swaps)
-//    by the chunk's own producer, so a chunk never waits for another
-//    producer.  Results go to a ring of LDS slots.
+//    Qt, Ki and the V slice in LDS, A_kk^T and A_qk^T on MFMA.  Each chunk's
+//    16 x 16 unit triangular system is solved by its own producer, by
+//    forward substitution in registers (a lane holds one row; the finished
+//    row is broadcast within a 16-lane row by DPP), so a chunk never waits
+//    for another producer.  Results go to a ring of LDS slots.
 //  * Consumer waves (one per 16 value columns) hold their columns of the fp32
 //    state in MFMA accumulators for the whole sequence; the state chain of a
 //    chunk (V - Kt S, Qt S, M' R, A_qk U, Ki^T U, decay) is wave-local, so
@@ -112,17 +112,21 @@ struct PipeCfg {
     static constexpr int SLOT = O_GM + 512;
     static constexpr int RING = kRing * SLOT;
     // behind the ring, one of two per-slot areas:
-    //  * (conv inputs) the triangular-inverse scratch: the 16 columns of -N
-    //    (16 floats each) and beta of the slot's chunk;
-    //  * (the others, which move those values with permlane swaps) the
-    //    chunk's output rows, 16 tokens x this workgroup's value columns in
-    //    bf16, gathered from the consumers and stored to memory whole
+    //  * the triangular solve's scratch: the 16 rows of -N in fp32, 80 bytes
+    //    apart (a lane's 16-byte reads of rows 0..15 then use all 64 banks
+    //    once);
+    //  * (with output staging) the chunk's output rows, 16 tokens x this
+    //    workgroup's value columns in bf16, gathered from the consumers and
+    //    stored to memory whole.  It doubles as the solve's scratch: the
+    //    slot's producer stores the previous rows before its solve, and the
+    //    consumers write the next ones after its publication.
+    static constexpr int PN = 80;
     static constexpr int O_NB = RING;
-    static constexpr int O_BT = O_NB + kRing * 16 * 16 * 4;
-    static constexpr int SCRATCH = kRing * (16 * 16 * 4 + 16 * 4);
+    static constexpr int SCRATCH = kRing * 16 * PN;
     static constexpr int PO = DVS * 2 + 16;             // output row pitch: rows 36 words apart
     static constexpr int O_OS = RING;
     static constexpr int STAGE = kRing * 16 * PO;
+    static_assert(16 * PN <= 16 * PO, "solve scratch inside a slot's staging rows");
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
@@ -167,68 +171,47 @@ __device__ __forceinline__ float row_bcast(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
                                                               0x150 + N, 0xF, 0xF, true));
 }
-// y += (lane M of the row's n) * m, one v_fmac_f32 with a DPP row broadcast
-// on its first source.  The broadcast operand must not be written by a VALU
-// instruction in the two instructions before (see back_subst_split).
+// Forward substitution for X = (I + N)^{-1} diag(beta), N strictly lower
+// triangular, one chunk per wave.  Lane (q, r) holds row r of -N in nn[] and
+// X[r][4q .. 4q+3] in x[] (started at diag(beta)).  Row M of X is final once
+// the steps before it are done; step M adds -N[r][M] X[M][.] to every row r,
+// the finished row coming from lane M of the lane's own 16-lane row by a DPP
+// broadcast folded into the multiply-add (rows r <= M add a masked zero).
+// 60 multiply-adds, written as asm: the compiler does not fold a broadcast
+// whose source is the accumulator itself (it adds a DPP move and a wait).
+// The four of a step are independent and keep their order (volatile asm), so
+// each broadcast read lies three instructions after the write of its
+// operand; forward_rows puts the wait states ahead of the first step.  Step
+// 15 would change no row and is left out.
 template <int M>
-__device__ __forceinline__ void fmac_bcast(float& y, float n, float m) {
-    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(y)
-                 : "v"(n), "v"(m), "i"(M));
-}
-
-// Row exchanges between two registers (gfx950 permlane swaps; both registers
-// are read and written): swap32 trades rows 2, 3 of a for rows 0, 1 of b,
-// swap16 the odd rows of a for the even rows of b.  Written as asm: the
-// compiler's builtin lost the second register's result when the two operands
-// differed.  The s_nop gives a swap the wait states after the VALU write of
-// its operands (its results need none: the compiler's own swaps are read at
-// once).
-__device__ __forceinline__ void swap32(float& a, float& b) {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap16(float& a, float& b) {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-// Lane c of row q of x, for every row q: row R of x broadcast to all four
-// 16-lane rows (R compile-time).
-template <int R>
-__device__ __forceinline__ float rows_bcast(float x) {
-    float a = x, b = x;
-    swap16(a, b);                 // a: rows 0, 0, 2, 2   b: rows 1, 1, 3, 3
-    float c = (R & 1) ? b : a, d = c;
-    swap32(c, d);                 // c: rows (R&1) twice   d: rows 2 + (R&1) twice
-    return (R & 2) ? d : c;
-}
-
-// Back substitution for Y = (I + N)^{-1}, N strictly upper triangular, split
-// over the four 16-lane rows (one chunk per wave): with Y - I = -N - N(Y - I)
-// solved column by column, entry M of a column is final once the entries
-// above it are done, and it updates every row r < M with -N[r][M].  Lane c
-// of row q holds rows r = q + 4k (k = 0..3) of column c, of -N in np[k] and
-// of Y in y[k] (started at column c of I, so Y comes out with its diagonal).
-// Step M broadcasts the finished entry Y[M][c] from its owner row (M % 4,
-// slot M / 4; two permlane swaps) and updates the slots k < ceil(M / 4) of
-// every row:
-// the rows r >= M among them add -N[r][M] = 0 (the masked entries are stored
-// as zeros).  36 broadcast multiply-adds in all.  np is complete before the
-// first broadcast read (the s_nop consumes it and adds the DPP read wait
-// states).
-template <int M>
-__device__ __forceinline__ void back_subst_split_steps(float (&y)[4], const float (&np)[4],
-                                                       int lr) {
-    if constexpr (M >= 1) {
-        // row M % 4 to all four rows (two permlane swaps, no LDS round trip)
-        const float piv = rows_bcast<M & 3>(y[M / 4]);
+__device__ __forceinline__ void forward_step(float (&x)[4], float n) {
+    if constexpr (M < 15) {
 #pragma unroll
-        for (int k = 0; k < (M + 3) / 4; ++k) fmac_bcast<M>(y[k], np[k], piv);
-        back_subst_split_steps<M - 1>(y, np, lr);
+        for (int k = 0; k < 4; ++k)
+            asm volatile("v_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+                         : "+v"(x[k])
+                         : "v"(n), "i"(M));
     }
 }
-
-__device__ __forceinline__ void back_subst_split(float (&y)[4], const float (&np)[4], int lr) {
-    asm volatile("s_nop 1" ::"v"(np[0]), "v"(np[1]), "v"(np[2]), "v"(np[3]));
-    back_subst_split_steps<15>(y, np, lr);
+// Steps 4J .. 4J+3 with entries 4J .. 4J+3 of the row of -N.
+template <int J>
+__device__ __forceinline__ void forward_group(float (&x)[4], floatx4 n) {
+    forward_step<4 * J + 0>(x, n[0]);
+    forward_step<4 * J + 1>(x, n[1]);
+    forward_step<4 * J + 2>(x, n[2]);
+    forward_step<4 * J + 3>(x, n[3]);
+}
+// The whole solve from the lane's row of -N in LDS (16 floats at row).
+__device__ __forceinline__ void forward_rows(float (&x)[4], const char* row) {
+    const floatx4* r = reinterpret_cast<const floatx4*>(row);
+    const floatx4 a = r[0], b = r[1], c = r[2], d = r[3];
+    // the wait states before the first broadcast read of x (its VALU writes
+    // may be the instructions just before)
+    asm volatile("s_nop 1" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+    forward_group<0>(x, a);
+    forward_group<1>(x, b);
+    forward_group<2>(x, c);
+    forward_group<3>(x, d);
 }
 
 // Rows of the state tiles KT .. NKT-1 times their decay e^{G_15}: row i of
@@ -901,56 +884,25 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 pack4(4 * lq + 0 <= lr ? aqk[0] : 0.f, 4 * lq + 1 <= lr ? aqk[1] : 0.f,
                       4 * lq + 2 <= lr ? aqk[2] : 0.f, 4 * lq + 3 <= lr ? aqk[3] : 0.f);
 
-            // ---- Y = (I + N)^{-1}, N = diag(beta) A_kk ------------------------
-            // Column c = lr of -N holds -beta_c A_kk[c][r] for r < c; lane
-            // (q, c) has rows r = 4q+i (the tile holds -Kt, so akk[i] =
-            // -A_kk[c][4q+i]).  The solve wants lane row q to hold rows q + 4k
-            // (k = 0..3) of the column (see back_subst_split), and each row
-            // then writes its rows of M', scaled by beta_{4k+q}.
-            float np[4] = {4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
-                           4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
-            float bk[4];
-            if constexpr (CV) {
-                // conv inputs (fewer registers to spare): through this slot's
-                // scratch in LDS, with beta
-                float* col = reinterpret_cast<float*>(smem + Cfg::O_NB) + (s * 16 + lr) * 16;
-                float* bet = reinterpret_cast<float*>(smem + Cfg::O_BT) + s * 16;
-                *reinterpret_cast<floatx4*>(col + 4 * lq) = floatx4{np[0], np[1], np[2], np[3]};
-                if (lq == 0) bet[lr] = bl;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    np[k] = col[lq + 4 * k];
-                    bk[k] = bet[4 * k + lq];
-                }
-            } else {
-                // a 4 x 4 transpose of (lane row, slot) in two rounds of
-                // permlane swaps; beta_{4k+q} as lane 4a+q of each quad a (a
-                // quad permutation on row q alone), then lane 4k of the row
-                swap32(np[0], np[2]);
-                swap32(np[1], np[3]);
-                swap16(np[0], np[1]);
-                swap16(np[2], np[3]);
-                float bq = 0.f;
-                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0x00, 0x1, 0xF, false));
-                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0x55, 0x2, 0xF, false));
-                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0xAA, 0x4, 0xF, false));
-                bq = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bq), __builtin_bit_cast(int, bl), 0xFF, 0x8, 0xF, false));
-                bk[0] = row_bcast<0>(bq);
-                bk[1] = row_bcast<4>(bq);
-                bk[2] = row_bcast<8>(bq);
-                bk[3] = row_bcast<12>(bq);
-            }
+            // ---- M' = (I + N)^{-1} diag(beta), N = diag(beta) A_kk -----------
+            // Lane (q, c) holds -A_kk[c][4q+i] (the tile holds -Kt); masked to
+            // the strict lower triangle and scaled by beta_c (this lane's
+            // beta, token c), entries 4q .. 4q+3 of row c of -N.  Through the
+            // slot's scratch every lane then reads a whole row r = lr of -N
+            // and solves (I + N) X = diag(beta) for X[r][4q .. 4q+3], which is
+            // M' in the 16x16x16 A-operand layout (lane (q, r): row r,
+            // columns 4q .. 4q+3).
+            const floatx4 nq = {4 * lq + 0 < lr ? bl * akk[0] : 0.f, 4 * lq + 1 < lr ? bl * akk[1] : 0.f,
+                                4 * lq + 2 < lr ? bl * akk[2] : 0.f, 4 * lq + 3 < lr ? bl * akk[3] : 0.f};
             if (go) {
-                float y[4];
+                char* scr = smem + (kStageO ? Cfg::O_OS + s * 16 * Cfg::PO : Cfg::O_NB + s * 16 * Cfg::PN) +
+                            lr * Cfg::PN;
+                *reinterpret_cast<floatx4*>(scr + 16 * lq) = nq;
+                float x[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) y[k] = lq + 4 * k == lr ? 1.f : 0.f;
-                back_subst_split(y, np, lr);
-                // M'[lr][4k+q] = Y[4k+q][lr] beta_{4k+q}: entry q of the
-                // 4-entry group k of lane (k, lr) of the 16x16x16 A operand
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    *reinterpret_cast<__bf16*>(slot + Cfg::O_MP + (16 * k + lr) * 8 + lq * 2) =
-                        (__bf16)(y[k] * bk[k]);
+                for (int k = 0; k < 4; ++k) x[k] = lr == 4 * lq + k ? bl : 0.f;
+                forward_rows(x, scr);
+                *reinterpret_cast<shortx4*>(slot + Cfg::O_MP + lane * 8) = pack4(x[0], x[1], x[2], x[3]);
                 // publish the chunk after every lane's M' writes (the LDS
                 // performs this wave's operations in order; the release keeps
                 // the compiler from sinking the writes below it)
