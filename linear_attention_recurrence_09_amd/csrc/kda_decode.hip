@@ -53,6 +53,21 @@ __device__ __forceinline__ void stream_store(V v, V* p) {
 // registers).  Either way a thread's q, k and decays are 16-byte LDS reads.
 // The strided layout streams faster; the consecutive one keeps three
 // workgroups per CU, which pays once several tokens' arithmetic dominates.
+// Lane sums of the token loop: DPP and permlane steps (group_sum) in the
+// consecutive-row kernel, where the per-token work dominates; shuffles through
+// the LDS crossbar in the strided kernel, which streams the state for one or
+// two tokens and measured 1-2% faster with them.
+template <bool kXbar, int width>
+__device__ __forceinline__ float lane_sum(float v) {
+    if constexpr (kXbar) {
+#pragma unroll
+        for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+        return v;
+    } else {
+        return group_sum<width>(v);
+    }
+}
+
 template <typename T, int D, bool kStrided>
 __global__ void __launch_bounds__(kDecThreads)
 decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const T* cs_in,
@@ -143,7 +158,7 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
             w0[0] = w0[1]; w0[1] = w0[2]; w0[2] = x0;
             w1[0] = w1[1]; w1[1] = w1[2]; w1[2] = x1;
         }
-        float ss = group_sum<D / 2>(y0 * y0 + y1 * y1);
+        float ss = lane_sum<kStrided, D / 2>(y0 * y0 + y1 * y1);
         if (part < 2) {
             const float inv = rsqrt_nr(ss + l2_eps);
             y0 *= inv;
@@ -161,7 +176,7 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
         if (wave == 0) {   // k . q
             float kq = 0.f;
             for (int i = lane; i < D; i += 64) kq += su[i] * su[D + i];
-            kq = group_sum<64>(kq);
+            kq = lane_sum<kStrided, 64>(kq);
             if (lane == 0) skq = kq;
         }
 
@@ -182,17 +197,29 @@ decode_multi_kernel(const T* __restrict__ x, const float* __restrict__ w, const 
                 aq.x += qi * sv[j][0]; aq.y += qi * sv[j][1]; aq.z += qi * sv[j][2]; aq.w += qi * sv[j][3];
             }
         }
+        // Sum over the row groups of the wave (lanes cg, cg + CG, ...).  The
+        // 16-lane level (D = 64) keeps every sum in every lane; the 32-lane
+        // level swaps two sums at once, so lanes below 32 end with those of
+        // x and z and lanes from 32 on with those of y and w.
+        float pr[8] = {ak.x, ak.y, ak.z, ak.w, aq.x, aq.y, aq.z, aq.w};
+        if constexpr (CG == 16) {
 #pragma unroll
-        for (int m = CG; m < 64; m <<= 1) {
-            ak.x += __shfl_xor(ak.x, m, 64); ak.y += __shfl_xor(ak.y, m, 64);
-            ak.z += __shfl_xor(ak.z, m, 64); ak.w += __shfl_xor(ak.w, m, 64);
-            aq.x += __shfl_xor(aq.x, m, 64); aq.y += __shfl_xor(aq.y, m, 64);
-            aq.z += __shfl_xor(aq.z, m, 64); aq.w += __shfl_xor(aq.w, m, 64);
+            for (int e = 0; e < 8; ++e) {
+                float even = pr[e], odd = pr[e];
+                rows_swap16(even, odd);   // even: rows 0, 0, 2, 2   odd: rows 1, 1, 3, 3
+                pr[e] = even + odd;
+            }
         }
-        if (lane < CG) {
+        static_assert(CG == 16 || CG == 32, "row groups of the wave");
+        const int hw = lane >> 5;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            rows_swap32(pr[e], pr[e + 1]);
+            pr[e] += pr[e + 1];
+        }
+        if ((lane & 31) < CG) {
             float* r = sred[wave][cg];
-            r[0] = ak.x; r[1] = ak.y; r[2] = ak.z; r[3] = ak.w;
-            r[4] = aq.x; r[5] = aq.y; r[6] = aq.z; r[7] = aq.w;
+            r[hw] = pr[0]; r[2 + hw] = pr[2]; r[4 + hw] = pr[4]; r[6 + hw] = pr[6];
         }
         __syncthreads();
         float tk[4] = {0.f, 0.f, 0.f, 0.f}, tq[4] = {0.f, 0.f, 0.f, 0.f};

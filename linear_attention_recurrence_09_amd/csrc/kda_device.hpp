@@ -207,11 +207,47 @@ __device__ __forceinline__ float rsqrt_nr(float x) {
     return r * (1.5f - 0.5f * x * r * r);
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Row exchanges between two registers (gfx950 permlane swaps; both are read
+// and written): swap16 trades the odd 16-lane rows of a for the even rows of
+// b, swap32 rows 2, 3 of a for rows 0, 1 of b.  asm with the wait states for
+// the VALU writes of the operands ahead (the compiler's builtin lost the
+// second register's result when the operands differed).
+__device__ __forceinline__ void rows_swap16(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void rows_swap32(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64), the
+// same value in every lane of a group (each step adds two partial sums that
+// the paired lanes hold in swapped order).  Within a 16-lane row by DPP:
+// quad permutations for 2 and 4 lanes, the half-row and row mirrors for 8
+// and 16 (after the quad steps a lane and its mirror hold the sums of the
+// two halves); across rows by permlane swaps.  The whole wave must be
+// active.  (Lane shuffles through the LDS crossbar, ds_bpermute, cost an LDS
+// round trip per step.)
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+    static_assert(width >= 1 && width <= 64 && (width & (width - 1)) == 0, "group width");
+    if constexpr (width >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (width >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (width >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+    if constexpr (width >= 16) v += dpp_f<0x140>(v);  // row_mirror
+    if constexpr (width >= 32) {
+        float a = v, b = v;
+        rows_swap16(a, b);   // a: rows 0, 0, 2, 2   b: rows 1, 1, 3, 3
+        v = a + b;
+    }
+    if constexpr (width >= 64) {
+        float a = v, b = v;
+        rows_swap32(a, b);   // a: rows 0, 1, 0, 1   b: rows 2, 3, 2, 3
+        v = a + b;
+    }
     return v;
 }
 
