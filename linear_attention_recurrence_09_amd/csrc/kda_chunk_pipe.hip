@@ -732,20 +732,26 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                         ss[i] = keep + xchg(send);
                     }
                 };
-                auto bperm = [&](float x, int m) {
-                    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane ^ m) << 2), __builtin_bit_cast(int, x)));
-                };
                 auto dpp = [](float x, auto ctrl_c) {
                     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
                                                                               decltype(ctrl_c)::value, 0xF, 0xF, true));
                 };
-                using I32 = std::integral_constant<int, 32>;
-                using I16 = std::integral_constant<int, 16>;
                 using I8 = std::integral_constant<int, 8>;
                 using I4 = std::integral_constant<int, 4>;
                 using I2 = std::integral_constant<int, 2>;
-                step(I32{}, 32, [&](float x) { return bperm(x, 32); });
-                step(I16{}, 16, [&](float x) { return bperm(x, 16); });
+                // the 32- and 16-lane steps are one permlane swap per pair: after
+                // swapping, each lane holds its own kept value and the partner's
+                // copy of it
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    rows_swap32(ss[i], ss[i + 16]);
+                    ss[i] += ss[i + 16];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    rows_swap16(ss[i], ss[i + 8]);
+                    ss[i] += ss[i + 8];
+                }
                 step(I8{}, 8, [&](float x) { return dpp(x, std::integral_constant<int, 0x128>{}); });   // row_ror:8
                 step(I4{}, 4, [&](float x) { return dpp(x, std::integral_constant<int, 0x141>{}); });   // row_half_mirror
                 step(I2{}, 2, [&](float x) { return dpp(x, std::integral_constant<int, 0x4E>{}); });    // quad_perm 2,3,0,1
