@@ -55,6 +55,36 @@ __device__ __forceinline__ bf16v4 mla_read_tr(const __bf16* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16v4_ptr)(p));
 }
 
+// One row of 64 x 16 bytes from memory into LDS: lane l's 16 bytes at g land
+// at lds_row + 16 l.  Issued as asm: the compiler does not count these loads,
+// so it adds no wait for them before the LDS reads; the caller waits
+// (vmcnt, then a barrier) before any wave reads the row.  lds_row is
+// wave-uniform; M0 carries it (one wait state before the load reads it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_row_load(const char* lds_row, const void* g) {
+    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_row;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m), "v"(g)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most n of this wave's loads are in flight.
+template <int n>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+}
+// Wait until at most min(after, A) tiles of RPL loads each are in flight.
+template <int RPL, int A>
+__device__ __forceinline__ void wait_tiles_in_flight(int after) {
+    if constexpr (A == 0) {
+        wait_loads<0>();
+    } else {
+        if (after >= A) wait_loads<A * RPL>();
+        else wait_tiles_in_flight<RPL, A - 1>(after);
+    }
+}
+
 // ---- 1. absorb: q'[b][h][r] = s * sum_d q[b][h][d] W_uk[h][d][r] ----------
 // Workgroup (head h, 32 sequences), 4 waves: a 32 x 512 x 128 product on
 // 16x16x32 MFMA.  W_uk[h] (128 x 512) is staged in LDS and read as the B
@@ -141,8 +171,11 @@ mla_absorb_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ w_uk,
 // [column]) is read in the same order by two transposed reads.  Softmax: a
 // running max per head (base 2: q' carries log2 e); row sums stay per lane
 // until the end.
-// Cache tiles stream through registers a step ahead into two LDS stages.
-constexpr int kCP = kR * 2 + 16;            // LDS row pitch (bytes) of a cache tile: 4 banks between rows
+// Cache tiles go straight from memory into a ring of four LDS stages, three
+// tiles ahead of the one being read (global loads with an LDS destination,
+// issued by up to eight loader waves, one 1 KB row per instruction).
+constexpr int kCP = kR * 2 + 32;            // LDS row pitch (bytes) of a cache tile: 8 banks between rows
+constexpr int kStages = 4;                  // LDS stages of cache tiles (>= 2)
 
 template <int HT>
 __global__ void __launch_bounds__(128 * HT)
@@ -150,9 +183,9 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
                 const int32_t* __restrict__ lengths, float* __restrict__ part_ml,
                 float* __restrict__ part_u, int Lmax, int nsplit) {
     constexpr int H = 16 * HT, NW = 2 * HT;
-    constexpr int RPW = (kTL + NW - 1) / NW;   // cache rows loaded per wave and tile
-    constexpr int SROWS = NW * RPW;            // rows of a stage (those past the tile are padding)
-    __shared__ __attribute__((aligned(16))) char sC[2][SROWS * kCP];
+    constexpr int NL = NW >= 8 ? 8 : (NW >= 4 ? 4 : 2);   // loader waves
+    constexpr int RPL = kTL / NL;                        // rows per loader wave and tile
+    __shared__ __attribute__((aligned(16))) char sC[kStages][kTL * kCP];
     __shared__ __attribute__((aligned(16))) floatx4 sX[NW][2][64];   // partial scores
     __shared__ __attribute__((aligned(16))) float sA[NW][16];        // rescale factors
 
@@ -179,28 +212,27 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
     asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]), "v"(qb[4]), "v"(qb[5]),
                  "v"(qb[6]), "v"(qb[7]));
 
-    // rows wave + NW j of a tile, 16 bytes per lane.  Every wave loads and
-    // stores the same number of rows with no branch (so the compiler counts
-    // the loads in flight exactly): rows past the tile land in the stage's
-    // padding rows, rows past the length repeat the last valid row (their
-    // scores are masked), and tiles past the range repeat the last tile
-    // (never used), so every load is in bounds.
+    // Loader wave w (< NL) loads rows w + NL j of a tile, 16 bytes per lane;
+    // rows past the length repeat the last valid row (their scores are
+    // masked), so every load is in bounds.  Tiles past the range are not
+    // loaded; the waits count only the tiles issued.
     const __bf16* cb = cache + (int64_t)b * Lmax * kR + 8 * lane;
-    auto fetch = [&](bf16x8 (&r)[RPW], int t) {
-        const int tc = t < t_hi ? t : t_hi - 1;
+    const bool loader = wave < NL;
+    auto issue = [&](int t) {
+        if (loader && t < t_hi) {
+            const char* st = sC[(t - t_lo) % kStages];
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
-            const int row = wave + NW * j;
-            int tok = tc * kTL + (row < kTL ? row : kTL - 1);
-            tok = tok < L ? tok : L - 1;
-            r[j] = *reinterpret_cast<const bf16x8*>(cb + (int64_t)tok * kR);
+            for (int j = 0; j < RPL; ++j) {
+                const int row = wave + NL * j;
+                int tok = t * kTL + row;
+                tok = tok < L ? tok : L - 1;
+                lds_row_load(st + row * kCP, cb + (int64_t)tok * kR);
+            }
         }
     };
-    auto put = [&](const bf16x8 (&r)[RPW], char* st) {
-#pragma unroll
-        for (int j = 0; j < RPW; ++j)
-            *reinterpret_cast<bf16x8*>(st + (wave + NW * j) * kCP + 16 * lane) = r[j];
-    };
+    // tile t has landed in this wave's rows once only the tiles issued after
+    // it (at most kStages - 2, none past the range) may still be in flight
+    auto wait_tile = [&](int t) { wait_tiles_in_flight<RPL, kStages - 2>(t_hi - 1 - t); };
 
     float m_ref = -__builtin_inff();   // per head (lane's c), identical over q
     float l_part = 0.f;                // this lane's share of the row sum
@@ -208,9 +240,13 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
 #pragma unroll
     for (int j = 0; j < 16; ++j) U[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // one tile on stage st; afterwards tile t + 2 (in flight in r since the
-    // previous step) goes into st and r is refilled with tile t + 3
-    auto step = [&](int t, char* st, bf16x8 (&r)[RPW]) {
+    // one tile on stage st.  The barrier ahead of it finds tile t in LDS and
+    // every wave done with the previous step, whose stage then takes tile
+    // t + kStages - 1
+    auto step = [&](int t, const char* st) {
+        wait_tile(t);
+        __syncthreads();
+        issue(t + kStages - 1);
         // this wave's half of S^T = C Q'^T for the two 16-token halves
         floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
@@ -275,21 +311,11 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
             U[j] = mla_mfma32(pa, cf, U[j]);
             if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
         }
-        __syncthreads();   // every wave is done with this stage and with sX
-        put(r, st);        // tile t + 2
-        fetch(r, t + 3);
     };
 
-    bf16x8 ra[RPW];
-    if (t_lo < t_hi) {
-        fetch(ra, t_lo);
-        put(ra, sC[0]);
-        fetch(ra, t_lo + 1);
-        put(ra, sC[1]);
-        fetch(ra, t_lo + 2);
-        __syncthreads();
-    }
-    for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) & 1], ra);
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) issue(t_lo + i);
+    for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) % kStages]);
 
     // partial results of this split: m, l per head; U [H][512]
     float l_head = l_part + __shfl_xor(l_part, 16, 64);
