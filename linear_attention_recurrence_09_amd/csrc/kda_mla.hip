@@ -176,6 +176,7 @@ mla_absorb_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ w_uk,
 // issued by up to eight loader waves, one 1 KB row per instruction).
 constexpr int kCP = kR * 2 + 32;            // LDS row pitch (bytes) of a cache tile: 8 banks between rows
 constexpr int kStages = 4;                  // LDS stages of cache tiles (>= 2)
+constexpr float kLazyMax = 8.f;             // growth of a head's max (base 2) before a rescale
 
 template <int HT>
 __global__ void __launch_bounds__(128 * HT)
@@ -264,21 +265,34 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
         s0 += sX[wave ^ 1][0][lane];
         s1 += sX[wave ^ 1][1][lane];
         // mask tokens past the length (only the last tile has any)
-        const int base = t * kTL + 4 * lq;
+        if (t * kTL + kTL > L) {
+            const int base = t * kTL + 4 * lq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (base + i >= L) s0[i] = -__builtin_inff();
-            if (base + 16 + i >= L) s1[i] = -__builtin_inff();
+            for (int i = 0; i < 4; ++i) {
+                if (base + i >= L) s0[i] = -__builtin_inff();
+                if (base + 16 + i >= L) s1[i] = -__builtin_inff();
+            }
         }
         float mt = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                          fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        // running max per head; U and the partial sums are rescaled every
-        // tile (the factor is 1 where the max did not move, 0 on the first
-        // tile, where m_ref starts at -inf)
         {
-            const float m_new = fmaxf(m_ref, mt);
+            float a = mt, b = mt;
+            rows_swap16(a, b);
+            mt = fmaxf(a, b);
+            a = mt;
+            b = mt;
+            rows_swap32(a, b);
+            mt = fmaxf(a, b);
+        }
+        // Lazy running max per head: a head's reference moves only when a
+        // tile's max exceeds it by more than kLazyMax (base 2), so U and the
+        // partial sums are rescaled on few tiles (any finite max moves the
+        // -inf of the first tile, where the factor is 0).  Between moves the
+        // probabilities stay below 2^kLazyMax.  Both waves of a head tile hold
+        // the same scores, hence take the same decisions.
+        const bool move = mt > m_ref + kLazyMax;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float m_new = move ? mt : m_ref;
             const float alpha = fast_exp2(m_ref - m_new);
             m_ref = m_new;
             l_part *= alpha;
@@ -318,8 +332,16 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
     for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) % kStages]);
 
     // partial results of this split: m, l per head; U [H][512]
-    float l_head = l_part + __shfl_xor(l_part, 16, 64);
-    l_head += __shfl_xor(l_head, 32, 64);
+    float l_head;
+    {
+        float a = l_part, b = l_part;
+        rows_swap16(a, b);
+        l_head = a + b;
+        a = l_head;
+        b = l_head;
+        rows_swap32(a, b);
+        l_head = a + b;
+    }
     const int64_t pb = ((int64_t)b * nsplit + sp) * H;
     if (hf == 0 && lq == 0) {
         part_ml[(pb + ht * 16 + lr) * 2] = m_ref;
