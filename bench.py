@@ -433,8 +433,8 @@ def cpu_baseline(inp, spec, T_s, H_s, gpu_out):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--cpu-heads", type=int, default=48)

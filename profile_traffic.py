@@ -3,9 +3,9 @@
 Inputs (CSV files written by the commands recorded in the summaries):
   --trace  <dir>/bench_kernel_stats.csv   from
            rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- \
-               python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline
+               python3 bench.py --steps 20 --warmup 10 --no-cpu-baseline
            (the per-dispatch <dir>/bench_kernel_trace.csv beside it gives the
-           average over the timed steps, the last 10 chunk-kernel dispatches)
+           average over the 20 timed steps of the headline workload)
   --fetch  <dir>/fetch_counter_collection.csv from
            rocprofv3 --pmc FETCH_SIZE -T -f csv -d <dir> -o fetch -- python3 bench.py --counters
   --write  <dir>/write_counter_collection.csv from
@@ -123,7 +123,7 @@ def main():
     lines = ["# rocprofv3 kernel statistics of one bench.py run (prefill T=65536, H=96, D=128,",
              "# bf16 I/O; decode B=256 x 64 steps; latent-attention decode B=256 x 4096), MI355X",
              "# command: rocprofv3 --kernel-trace --stats -T -f csv -d <dir> -o bench -- "
-             "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+             "python3 bench.py --steps 20 --warmup 10 --no-cpu-baseline",
              f"{'kernel':60s} {'calls':>6s} {'avg_ms':>10s} {'min_ms':>10s} {'max_ms':>10s} {'pct':>6s}"]
     for r in rows:
         lines.append(f"{r['Name'][:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e6:10.4f} "
@@ -134,7 +134,7 @@ def main():
     # for the headline workload (T=65536) first, then as often for each of the
     # other two prefill workloads; the headline's timed steps are launches
     # WARMUP .. WARMUP + STEPS - 1
-    WARMUP, STEPS = 2, 10
+    WARMUP, STEPS = 10, 20
     ktrace = os.path.join(os.path.dirname(args.trace), "bench_kernel_trace.csv")
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
             for r in csv.DictReader(open(ktrace)) if CHUNK_TAG in r["Kernel_Name"]]
