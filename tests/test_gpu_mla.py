@@ -1,8 +1,9 @@
 """kda_mla_decode on the GPU against the oracle's gated latent-attention decode
 step: every head count the kernel is built for, ragged cache lengths across
-tile and split boundaries, a near one-hot softmax, many tiles per split,
-clamped lengths, workspace reuse and determinism, and the 256-sequence x
-4096-token decode workload compared on sampled sequences."""
+tile and split boundaries, a near one-hot softmax, a running maximum that
+moves on later tiles, many tiles per split, clamped lengths, workspace reuse
+and determinism, and the 256-sequence x 4096-token decode workload compared
+on sampled sequences."""
 import numpy as np
 import pytest
 import torch
@@ -56,6 +57,26 @@ def test_mla_peaked_softmax():
     inp = synth.mla_inputs(spec, device="cuda", lengths=[70, 129, 300])
     y = _run(inp)
     assert report("y", f64(y), _oracle(inp), TOL_BF16) <= TOL_BF16
+
+
+def test_mla_running_max_moves_on_later_tiles():
+    """The kernel moves a head's softmax reference only when a tile's max
+    exceeds it by more than 2^8: cached latents that grow 16-fold along the
+    sequence (the max jumps by more than that on later tiles, so U is
+    rescaled mid-split) and latents that shrink (only the first tile moves
+    it).  64 sequences of 640 latents: 4 splits of 5 tiles each."""
+    print("mla running max: growing and shrinking latents", flush=True)
+    spec = synth.MlaSpec("mla_grow", B=64, H=96, L_max=640, seed=3601)
+    inp = synth.mla_inputs(spec, device="cuda")
+    t = torch.arange(640, device="cuda", dtype=torch.float32)
+    grow = 1.0 + 15.0 * t / 639.0
+    fac = torch.ones((64, 640), device="cuda")
+    fac[0::2] = grow
+    fac[1::2] = grow.flip(0)
+    inp["cache"] = (inp["cache"].float() * fac[:, :, None]).to(torch.bfloat16)
+    y = _run(inp)
+    seqs = [0, 1, 62, 63]
+    assert report("y (sampled)", f64(y[seqs]), _oracle(inp, seqs=seqs), TOL_BF16) <= TOL_BF16
 
 
 def test_mla_many_tiles_per_split():
