@@ -349,6 +349,11 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
     // (no room for the staging area beside the scratch and the taps)
     constexpr bool kStageO = SO;
     static_assert(!SO || !CV, "no output staging with conv inputs");
+    // A slot's staged rows are stored by the producer that refills it, and
+    // the last rows of every slot by the producer of that slot's last chunk
+    // (at its end): right only with one slot per producer, so that the last
+    // kNP chunks are the producers' last chunks and sit in distinct slots.
+    static_assert(!SO || kRing == kNP, "output staging needs one slot per producer");
     constexpr int O_W = Cfg::RING + (kStageO ? Cfg::STAGE : Cfg::SCRATCH);
     constexpr int WBYTES = CV ? (2 * DK + DVS) * 16 : 0;
     static_assert(O_W + WBYTES <= 160 * 1024 - 256, "LDS budget");
