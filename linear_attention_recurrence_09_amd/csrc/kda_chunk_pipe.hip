@@ -997,10 +997,6 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
         vv = lds_read_tr(slot + Cfg::O_V + tr_row * Cfg::PV + (16 * w + tr_col) * 2);
         mp = *reinterpret_cast<const shortx4*>(slot + Cfg::O_MP + lane * 8);
     };
-    // the 16x16x16 identity as an A operand (lane (q, r): row r, k = 4q+e)
-    shortx4 ident;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ident[e] = lr == 4 * lq + e ? (short)0x3F80 : (short)0;
     bool ok = nch == 0 || wait_at_least(&ready[0], 1, stop);
     // the slot is read only after its counter was seen (the compiler keeps
     // the reads below this point; the LDS serves a wave's operations in order)
@@ -1039,9 +1035,13 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
                 sb[ks][4 + e] = (__bf16)S[2 * ks + 1][e];
             }
         // R = V - Kt S (the state chain) first, then O^T = S^T Qt^T, which
-        // fills the wait for R.  V enters through an identity product (its
-        // transposed read is the 16x16x16 B layout) and the Kt tile holds -Kt.
-        floatx4 z = mfma16(ident, __builtin_bit_cast(shortx4, vv), zero4());
+        // fills the wait for R.  V is the chain's initial accumulator (its
+        // transposed read is the accumulator layout; bf16 to fp32 is exact)
+        // and the Kt tile holds -Kt.  (V no longer enters through a 16x16x16
+        // identity product: a 16x16x16 result read as the accumulator of a
+        // 16x16x32 product with no wait states between them came out wrong
+        // on gfx950, and the compiler puts none there.)
+        floatx4 z = {(float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) z = mfma32(fk[ks], sb[ks], z);
         __builtin_amdgcn_sched_barrier(0);
@@ -1056,7 +1056,11 @@ chunk_pipe_kernel(const typename PipeIn<IN>::type* __restrict__ q,
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) S[kt] = mfma16(__builtin_bit_cast(shortx4, ki[kt]), ub, S[kt]);
         // O^T += U^T A_qk^T: U's accumulator is the A operand of U^T, and the
-        // A_qk operand registers are the B operand of A_qk^T
+        // A_qk operand registers are the B operand of A_qk^T.  This 16x16x16
+        // product takes the 16x16x32 chain's O^T as its accumulator; the
+        // scheduling barriers keep the U product, the wait for its result and
+        // its packing between them (21 or more wait states in every
+        // instantiation).
         oa = mfma16(ub, aq, oa);
         // lane (q, t) holds O[t][16w + 4q .. +3]: 8 bytes of the chunk's output
         // rows, staged for the producer that refills this slot
