@@ -130,8 +130,8 @@ struct PipeCfg {
     static_assert(DK == 64 || DK == 128, "key width");
     static_assert(DVS == 64, "value slice");
     static_assert(SLOT % 16 == 0, "slot alignment");
-    // every producer keeps one slot (rings whose size does not divide the
-    // producer count gave wrong results in tests)
+    // the ring sizes that are built and tested: a divisor of the producer
+    // count (output staging needs exactly one slot per producer, below)
     static_assert(kNP % kRing == 0, "ring size divides the producer count");
 };
 
