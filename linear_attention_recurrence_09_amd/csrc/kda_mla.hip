@@ -347,6 +347,23 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
         part_ml[(pb + ht * 16 + lr) * 2] = m_ref;
         part_ml[(pb + ht * 16 + lr) * 2 + 1] = l_head;
     }
+    if (nsplit == 1) {
+        // one split: u = U / l itself, in bf16 (the combine step takes it as
+        // is); U's rows are heads 4q .. 4q+3, whose sums come through sA
+        if (lq == 0) sA[wave][lr] = l_head;
+        __builtin_amdgcn_wave_barrier();
+        const floatx4 lh = *reinterpret_cast<const floatx4*>(&sA[wave][4 * lq]);
+        float inv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) inv[i] = 1.f / lh[i];
+        __bf16* ub = reinterpret_cast<__bf16*>(part_u);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ub[(pb + ht * 16 + 4 * lq + i) * kR + 256 * hf + 16 * j + lr] = (__bf16)(U[j][i] * inv[i]);
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
@@ -378,52 +395,63 @@ mla_combine_kernel(const float* __restrict__ part_ml, const float* __restrict__ 
         wv[ks][0] = *reinterpret_cast<const bf16x8*>(wr + 32 * ks);
         wv[ks][1] = *reinterpret_cast<const bf16x8*>(wr + 16 * kR + 32 * ks);
     }
-    // merge the splits: wave w takes sequences b0 + 8 w .. +7, lane l latent
-    // columns 8 l .. 8 l + 7; splits outermost, so each split's loads for
-    // all eight sequences are in flight together
-    float M[8], den[8], num[8][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        M[j] = -__builtin_inff();
-        den[j] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) num[j][e] = 0.f;
-    }
     const int j0 = 8 * wave;
-    auto row_of = [&](int j) -> int64_t {   // sequences past B reuse b0's rows (never stored)
-        const int bb = b0 + j0 + j < B ? b0 + j0 + j : b0;
-        return (int64_t)bb * nsplit * H + h;
-    };
-    for (int sp = 0; sp < nsplit; ++sp)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) M[j] = fmaxf(M[j], part_ml[(row_of(j) + (int64_t)sp * H) * 2]);
-    for (int sp = 0; sp < nsplit; ++sp) {
-        floatx4 pu[8][2];
+    if (nsplit == 1) {
+        // one split: the attention step stored u = U / l in bf16 already
+        const __bf16* ub = reinterpret_cast<const __bf16*>(part_u);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float* src = part_u + (row_of(j) + (int64_t)sp * H) * kR + 8 * lane;
-            pu[j][0] = *reinterpret_cast<const floatx4*>(src);
-            pu[j][1] = *reinterpret_cast<const floatx4*>(src + 4);
+            bf16x8 v = {};
+            if (j0 + j < nb) v = *reinterpret_cast<const bf16x8*>(ub + ((int64_t)(b0 + j0 + j) * H + h) * kR + 8 * lane);
+            *reinterpret_cast<bf16x8*>(su + (j0 + j) * kUP + 16 * lane) = v;
         }
+    } else {
+        // merge the splits: wave w takes sequences b0 + 8 w .. +7, lane l latent
+        // columns 8 l .. 8 l + 7; splits outermost, so each split's loads for
+        // all eight sequences are in flight together
+        float M[8], den[8], num[8][8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t ps = row_of(j) + (int64_t)sp * H;
-            const float ws = fast_exp2(part_ml[ps * 2] - M[j]);   // 0 for an empty split
-            den[j] += ws * part_ml[ps * 2 + 1];
+            M[j] = -__builtin_inff();
+            den[j] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                num[j][e] += ws * pu[j][0][e];
-                num[j][4 + e] += ws * pu[j][1][e];
+            for (int e = 0; e < 8; ++e) num[j][e] = 0.f;
+        }
+        auto row_of = [&](int j) -> int64_t {   // sequences past B reuse b0's rows (never stored)
+            const int bb = b0 + j0 + j < B ? b0 + j0 + j : b0;
+            return (int64_t)bb * nsplit * H + h;
+        };
+        for (int sp = 0; sp < nsplit; ++sp)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) M[j] = fmaxf(M[j], part_ml[(row_of(j) + (int64_t)sp * H) * 2]);
+        for (int sp = 0; sp < nsplit; ++sp) {
+            floatx4 pu[8][2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float* src = part_u + (row_of(j) + (int64_t)sp * H) * kR + 8 * lane;
+                pu[j][0] = *reinterpret_cast<const floatx4*>(src);
+                pu[j][1] = *reinterpret_cast<const floatx4*>(src + 4);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t ps = row_of(j) + (int64_t)sp * H;
+                const float ws = fast_exp2(part_ml[ps * 2] - M[j]);   // 0 for an empty split
+                den[j] += ws * part_ml[ps * 2 + 1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    num[j][e] += ws * pu[j][0][e];
+                    num[j][4 + e] += ws * pu[j][1][e];
+                }
             }
         }
-    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float inv = j0 + j < nb ? 1.f / den[j] : 0.f;
-        bf16x8 v;
+        for (int j = 0; j < 8; ++j) {
+            const float inv = j0 + j < nb ? 1.f / den[j] : 0.f;
+            bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)(num[j][e] * inv);
-        *reinterpret_cast<bf16x8*>(su + (j0 + j) * kUP + 16 * lane) = v;
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)(num[j][e] * inv);
+            *reinterpret_cast<bf16x8*>(su + (j0 + j) * kUP + 16 * lane) = v;
+        }
     }
     __syncthreads();
     floatx4 acc[2][2];
