@@ -203,9 +203,11 @@ def main():
     ]
     # the latent-attention decode step (256 sequences x 4096 cached latents,
     # 96 heads, one split per sequence): each kernel against the bytes it must
-    # move, its split partials (m, l, U in fp32) included
+    # move, the hand-over between attention and combine included (with one
+    # split that is u = U / l in bf16; the (m, l) pair the attention kernel
+    # also writes, 0.2 MB, is counted as its own overhead)
     B, H, L, R, Dh = 256, 96, 4096, 512, 128
-    partials = B * H * (R + 2) * 4
+    partials = B * H * R * 2
     kinds += [
         ("latent attn: absorb (q' = W_uk^T q)", "mla_absorb_kernel",
          B * H * Dh * 2 + H * Dh * R * 2 + B * H * R * 2),
