@@ -225,11 +225,21 @@ conv_kernel(const T* __restrict__ x, const float* __restrict__ w, void* __restri
         }
     };
 
+    // the thread's taps, 8 channels x 4: 128 contiguous bytes in four-float
+    // loads (one float per load made as many L1-to-L2 requests as the data
+    // the strip streams); channels past P read as zeros, since the resource
+    // ends at channel P
     float wt[8][4];
+    {
+        const rsrc_t rw = make_rsrc(w + (int64_t)cbase * 4, (uint32_t)((P - cbase) * 16));
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e) {
+            const floatx4 v = __builtin_bit_cast(
+                floatx4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)threadIdx.x * 128 + 16 * e, 0, 0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wt[e][i] = active ? w[(c0 + e) * 4 + i] : 0.f;
+            for (int i = 0; i < 4; ++i) wt[e][i] = v[i];
+        }
+    }
 
     SeqRange sr = find_seq(cu, num_seqs, T_len, N, t0);
 
