@@ -14,7 +14,9 @@ Inputs (CSV files written by the commands recorded in the summaries):
 Writes profiles/chunk_prefill_T65536_kernel_stats.txt (every kernel of the
 run, the latent-attention decode kernels included),
 profiles/chunk_prefill_T65536_traffic.json and, for every kernel of the
-counter run, profiles/kernels_traffic_T65536_B256.txt.  The byte counters (KiB per
+counter run, profiles/kernels_traffic_T65536_B256.txt.  With --l2a/--l2b/--l2c
+(three L1/L2 counter passes, L2_PASSES) it writes the memory-path comparison of
+the streaming kernels, profiles/memory_path_T65536.txt.  The byte counters (KiB per
 dispatch) are scaled by what the same counter reads for bench.py's copy
 kernel of known size (2 GiB read, 2 GiB written); the JSON records the hash
 of the chunk-kernel sources so bench.py can tell whether it is current.
@@ -102,14 +104,95 @@ def pmc_summary(pmc1, pmc2, n_xcc=8, cu_active=192, simd_per_cu=4, chunks=4096):
     return lines
 
 
+L2_PASSES = [
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_WRREQ_STALL_sum TCC_TAG_STALL_sum "
+    "TCP_PENDING_STALL_CYCLES_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum "
+    "TCP_TCC_WRITE_REQ_sum GRBM_GUI_ACTIVE",
+    "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_WRREQ_sum "
+    "GRBM_GUI_ACTIVE",
+    "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum TCC_BUSY_sum "
+    "TCC_CYCLE_sum GRBM_GUI_ACTIVE",
+]
+# streaming kernels of the counter run compared on their memory path, with the
+# tag that finds each one's last dispatch
+L2_KERNELS = [
+    ("conv bf16 (kda_conv)", "conv_kernelIDF16bLi128ELb0E"),
+    ("conv MXFP8 out (kda_conv_mxfp8)", "conv_kernelIDF16bLi128ELb1E"),
+    ("gated norm (kda_gated_norm)", "gated_norm_kernel"),
+    ("copy, 2 GiB in + 2 GiB out", COPY_TAG),
+    ("chunk (kda_chunk_prefill)", CHUNK_TAG),
+    ("latent attention over the cache", "mla_attn_kernel"),
+]
+
+
+def memory_path_summary(l2a, l2b, l2c, n_xcc=8, n_cu=256, tcc_instances=128):
+    """L1 and L2 request counts, HBM latencies (Little's law: the summed
+    request level over the requests) and stall fractions of the streaming
+    kernels, from three counter passes of `bench.py --counters`."""
+    def last(path, tag):
+        d = counters_by_dispatch(path)
+        hits = [k for k in sorted(d) if tag in d[k][0]]
+        return d[hits[-1]][1] if hits else None
+
+    def times(path, tag):
+        t = {}
+        for r in csv.DictReader(open(path)):
+            if tag in r["Kernel_Name"]:
+                t[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6
+        return t[max(t)] if t else float("nan")
+
+    lines = ["# Memory path of the streaming kernels: rocprofv3 L1 (TCP) and L2 (TCC) counters, MI355X,",
+             "# last dispatch of each kernel in `python3 bench.py --counters`; three passes:"]
+    lines += [f"#   rocprofv3 --pmc {p} -T -f csv -d <dir> -o l2{'abc'[i]} -- python3 bench.py --counters"
+              for i, p in enumerate(L2_PASSES)]
+    lines += ["# cycles: GRBM_GUI_ACTIVE over the 8 XCCs (shader clock); L2 cycles: TCC_CYCLE over its",
+              f"# {tcc_instances} instances; latencies in L2 cycles; 'in flight' = requests outstanding at the",
+              "# L2-to-memory interface on average (chip-wide), 128-byte reads; L1 requests per cycle are per CU",
+              f"# over all {n_cu} CUs; 'L1 pending' = share of CU cycles the L1 waits on outstanding requests", "",
+              f"{'kernel':34s} {'ms':>6s} {'L1 rd req':>10s} {'L1 wr req':>10s} {'req/cyc/CU':>10s} "
+              f"{'L1 pending':>10s} {'L2 hit':>7s} {'rd lat':>7s} {'wr lat':>7s} {'rd in flight':>12s} "
+              f"{'DRAM rd/wr credit stall':>23s}"]
+    for label, tag in L2_KERNELS:
+        a, b, c = last(l2a, tag), last(l2b, tag), last(l2c, tag)
+        if not (a and b and c):
+            lines.append(f"{label:34s}  no dispatches")
+            continue
+        cyc = a["GRBM_GUI_ACTIVE"] / n_xcc
+        l2cyc = c["TCC_CYCLE_sum"] / tcc_instances
+        rd, wr = a["TCP_TCC_READ_REQ_sum"], a["TCP_TCC_WRITE_REQ_sum"]
+        lines.append(
+            f"{label:34s} {times(l2a, tag):6.3f} {rd:10.3e} {wr:10.3e} {(rd + wr) / cyc / n_cu:10.3f} "
+            f"{100 * a['TCP_PENDING_STALL_CYCLES_sum'] / cyc / n_cu:9.1f}% "
+            f"{100 * a['TCC_HIT_sum'] / (a['TCC_HIT_sum'] + a['TCC_MISS_sum']):6.1f}% "
+            f"{b['TCC_EA0_RDREQ_LEVEL_sum'] / b['TCC_EA0_RDREQ_sum']:7.0f} "
+            f"{b['TCC_EA0_WRREQ_LEVEL_sum'] / b['TCC_EA0_WRREQ_sum']:7.0f} "
+            f"{b['TCC_EA0_RDREQ_LEVEL_sum'] / l2cyc:12.0f} "
+            f"{100 * c['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / c['TCC_CYCLE_sum']:10.2f}% / "
+            f"{100 * c['TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum'] / c['TCC_CYCLE_sum']:.2f}%")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
     ap.add_argument("--pmc1", help="counter_collection.csv of the first counter pass (optional)")
     ap.add_argument("--pmc2", help="counter_collection.csv of the second counter pass")
+    ap.add_argument("--l2a", help="counter_collection.csv of the first L1/L2 pass (L2_PASSES)")
+    ap.add_argument("--l2b", help="... of the second")
+    ap.add_argument("--l2c", help="... of the third")
     args = ap.parse_args()
+    if args.l2a and args.l2b and args.l2c:
+        ml = memory_path_summary(args.l2a, args.l2b, args.l2c)
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        with open(os.path.join(ROOT, "profiles", "memory_path_T65536.txt"), "w") as f:
+            f.write("\n".join(ml) + "\n")
+        print("\n".join(ml))
+    if not (args.trace and args.fetch and args.write):
+        if not args.l2a:
+            ap.error("--trace, --fetch and --write are required (or the three --l2 passes)")
+        return
     import bench
     if args.pmc1 and args.pmc2:
         pl = pmc_summary(args.pmc1, args.pmc2)
