@@ -74,17 +74,6 @@ __device__ __forceinline__ void wait_loads() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
 }
-// Wait until at most min(after, A) tiles of RPL loads each are in flight.
-template <int RPL, int A>
-__device__ __forceinline__ void wait_tiles_in_flight(int after) {
-    if constexpr (A == 0) {
-        wait_loads<0>();
-    } else {
-        if (after >= A) wait_loads<A * RPL>();
-        else wait_tiles_in_flight<RPL, A - 1>(after);
-    }
-}
-
 // ---- 1. absorb: q'[b][h][r] = s * sum_d q[b][h][d] W_uk[h][d][r] ----------
 // Workgroup (head h, 32 sequences), 4 waves: a 32 x 512 x 128 product on
 // 16x16x32 MFMA.  W_uk[h] (128 x 512) is staged in LDS and read as the B
@@ -171,11 +160,12 @@ mla_absorb_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ w_uk,
 // [column]) is read in the same order by two transposed reads.  Softmax: a
 // running max per head (base 2: q' carries log2 e); row sums stay per lane
 // until the end.
-// Cache tiles go straight from memory into a ring of four LDS stages, three
-// tiles ahead of the one being read (global loads with an LDS destination,
-// issued by up to eight loader waves, one 1 KB row per instruction).
+// Cache tiles go straight from memory into a ring of three LDS stages (global
+// loads with an LDS destination, issued by up to eight loader waves, one 1 KB
+// row per instruction): while tile t is read, tile t+1 lands and tile t+2 is
+// issued.  One barrier per tile.
 constexpr int kCP = kR * 2 + 32;            // LDS row pitch (bytes) of a cache tile: 8 banks between rows
-constexpr int kStages = 4;                  // LDS stages of cache tiles (>= 2)
+constexpr int kStages = 3;                  // LDS stages of cache tiles: t, t+1 and t+2 in flight
 constexpr float kLazyMax = 8.f;             // growth of a head's max (base 2) before a rescale
 
 template <int HT>
@@ -187,7 +177,7 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
     constexpr int NL = NW >= 8 ? 8 : (NW >= 4 ? 4 : 2);   // loader waves
     constexpr int RPL = kTL / NL;                        // rows per loader wave and tile
     __shared__ __attribute__((aligned(16))) char sC[kStages][kTL * kCP];
-    __shared__ __attribute__((aligned(16))) floatx4 sX[NW][2][64];   // partial scores
+    __shared__ __attribute__((aligned(16))) floatx4 sX[2][NW][2][64];   // partial scores, by tile parity
     __shared__ __attribute__((aligned(16))) float sA[NW][16];        // rescale factors
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -231,23 +221,17 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
             }
         }
     };
-    // tile t has landed in this wave's rows once only the tiles issued after
-    // it (at most kStages - 2, none past the range) may still be in flight
-    auto wait_tile = [&](int t) { wait_tiles_in_flight<RPL, kStages - 2>(t_hi - 1 - t); };
-
     float m_ref = -__builtin_inff();   // per head (lane's c), identical over q
     float l_part = 0.f;                // this lane's share of the row sum
     floatx4 U[16];                     // lane (q, c): heads 4q+i, column 256 hf + 16 j + c
 #pragma unroll
     for (int j = 0; j < 16; ++j) U[j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // one tile on stage st.  The barrier ahead of it finds tile t in LDS and
-    // every wave done with the previous step, whose stage then takes tile
-    // t + kStages - 1
+    // One barrier per tile.  Before it each wave has written its partial
+    // scores of tile t (double-buffered by tile parity) and waited for its
+    // own rows of tile t+1; after it tile t+1 is in LDS for everyone, every
+    // wave is done with tile t-1's stage, which then takes tile t+2
     auto step = [&](int t, const char* st) {
-        wait_tile(t);
-        __syncthreads();
-        issue(t + kStages - 1);
         // this wave's half of S^T = C Q'^T for the two 16-token halves
         floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
@@ -259,11 +243,13 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
             s1 = mla_mfma32(a1, qb[ks], s1);
             if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
         }
-        sX[wave][0][lane] = s0;
-        sX[wave][1][lane] = s1;
-        __syncthreads();   // both halves of every head tile's scores are in LDS
-        s0 += sX[wave ^ 1][0][lane];
-        s1 += sX[wave ^ 1][1][lane];
+        sX[t & 1][wave][0][lane] = s0;
+        sX[t & 1][wave][1][lane] = s1;
+        wait_loads<0>();   // this wave's rows of tile t+1 (the last issued)
+        __syncthreads();
+        issue(t + 2);
+        s0 += sX[t & 1][wave ^ 1][0][lane];
+        s1 += sX[t & 1][wave ^ 1][1][lane];
         // mask tokens past the length (only the last tile has any)
         if (t * kTL + kTL > L) {
             const int base = t * kTL + 4 * lq;
@@ -327,8 +313,10 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
         }
     };
 
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i) issue(t_lo + i);
+    issue(t_lo);
+    issue(t_lo + 1);
+    if (t_lo + 1 < t_hi) wait_loads<RPL>(); else wait_loads<0>();
+    __syncthreads();
     for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) % kStages]);
 
     // partial results of this split: m, l per head; U [H][512]
