@@ -231,9 +231,11 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
     // scores of tile t (double-buffered by tile parity) and waited for its
     // own rows of tile t+1; after it tile t+1 is in LDS for everyone, every
     // wave is done with tile t-1's stage, which then takes tile t+2
-    auto step = [&](int t, const char* st) {
-        // this wave's half of S^T = C Q'^T for the two 16-token halves
-        floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    // this wave's half of S^T = C Q'^T for the two 16-token halves of the
+    // tile on stage st
+    auto scores = [&](const char* st, floatx4& s0, floatx4& s1) {
+        s0 = floatx4{0.f, 0.f, 0.f, 0.f};
+        s1 = s0;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int off = (256 * hf + 32 * ks + 8 * lq) * 2;
@@ -243,11 +245,16 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
             s1 = mla_mfma32(a1, qb[ks], s1);
             if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
         }
-        sX[t & 1][wave][0][lane] = s0;
-        sX[t & 1][wave][1][lane] = s1;
-        wait_loads<0>();   // this wave's rows of tile t+1 (the last issued)
-        __syncthreads();
-        issue(t + 2);
+    };
+    floatx4 c0, c1;   // this wave's partial scores of the current tile
+    // One barrier per tile.  Ahead of barrier t each wave has written its
+    // partial scores of tile t (double-buffered by tile parity) and waited for
+    // its own rows of tile t+1; after it tile t+1 is in LDS for everyone, every
+    // wave is done with tile t-1's stage, which then takes tile t+2.  Tile
+    // t+1's scores are formed right after the barrier, beside tile t's softmax.
+    auto step = [&](int t, const char* st) {
+        floatx4 s0 = c0, s1 = c1;
+        if (t + 1 < t_hi) scores(sC[(t + 1 - t_lo) % kStages], c0, c1);
         s0 += sX[t & 1][wave ^ 1][0][lane];
         s1 += sX[t & 1][wave ^ 1][1][lane];
         // mask tokens past the length (only the last tile has any)
@@ -311,12 +318,27 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
             U[j] = mla_mfma32(pa, cf, U[j]);
             if (j % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
         }
+        if (t + 1 < t_hi) {
+            sX[(t + 1) & 1][wave][0][lane] = c0;
+            sX[(t + 1) & 1][wave][1][lane] = c1;
+            wait_loads<0>();   // this wave's rows of tile t+2 (the last issued)
+            __syncthreads();
+            issue(t + 3);
+        }
     };
 
     issue(t_lo);
     issue(t_lo + 1);
     if (t_lo + 1 < t_hi) wait_loads<RPL>(); else wait_loads<0>();
-    __syncthreads();
+    __syncthreads();   // tile t_lo in LDS
+    if (t_lo < t_hi) {
+        scores(sC[0], c0, c1);
+        sX[t_lo & 1][wave][0][lane] = c0;
+        sX[t_lo & 1][wave][1][lane] = c1;
+        wait_loads<0>();   // tile t_lo + 1
+        __syncthreads();
+        issue(t_lo + 2);
+    }
     for (int t = t_lo; t < t_hi; ++t) step(t, sC[(t - t_lo) % kStages]);
 
     // partial results of this split: m, l per head; U [H][512]
