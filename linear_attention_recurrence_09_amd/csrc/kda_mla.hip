@@ -388,6 +388,10 @@ mla_attn_kernel(const __bf16* __restrict__ qp, const __bf16* __restrict__ cache,
 // the A operand, rows of W_uv[h] the B operand straight from memory (K = the
 // latent index runs along them).  Wave w owns output columns 32 w .. +31.
 constexpr int kUP = kR * 2 + 16;   // LDS row pitch (bytes) of u
+// MERGE: several splits to merge; without it (one split) the kernel only
+// copies u, and leaves out the merge's registers, which would otherwise hold
+// it to one wave per SIMD
+template <bool MERGE>
 __global__ void __launch_bounds__(256)
 mla_combine_kernel(const float* __restrict__ part_ml, const float* __restrict__ part_u,
                    const __bf16* __restrict__ w_uv, const __bf16* __restrict__ gate,
@@ -406,7 +410,7 @@ mla_combine_kernel(const float* __restrict__ part_ml, const float* __restrict__ 
         wv[ks][1] = *reinterpret_cast<const bf16x8*>(wr + 16 * kR + 32 * ks);
     }
     const int j0 = 8 * wave;
-    if (nsplit == 1) {
+    if constexpr (!MERGE) {
         // one split: the attention step stored u = U / l in bf16 already
         const __bf16* ub = reinterpret_cast<const __bf16*>(part_u);
 #pragma unroll
@@ -566,8 +570,12 @@ hipError_t launch_mla_decode(const void* q, const void* w_uk, const void* w_uv,
         default: e = launch_attn_t<6>(qp, cache, lengths, ml, pu, B, Lmax, ns, s); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, grid_bh, dim3(256), 0, s, ml, pu, (const __bf16*)w_uv,
-                       (const __bf16*)gate, (__bf16*)y, B, H, ns);
+    if (ns == 1)
+        hipLaunchKernelGGL(mla_combine_kernel<false>, grid_bh, dim3(256), 0, s, ml, pu,
+                           (const __bf16*)w_uv, (const __bf16*)gate, (__bf16*)y, B, H, ns);
+    else
+        hipLaunchKernelGGL(mla_combine_kernel<true>, grid_bh, dim3(256), 0, s, ml, pu,
+                           (const __bf16*)w_uv, (const __bf16*)gate, (__bf16*)y, B, H, ns);
     return hipGetLastError();
 }
 
